@@ -1,0 +1,139 @@
+/*
+ * nrc.h - C ABI of libnrc, the MI355X (gfx950) context K/V chain of the
+ * DSpark draft: hidden RMSNorm -> per-layer input RMSNorm, stacked -> batched
+ * K/V projection -> weightless 64-wide K-norm -> GPT-J RoPE -> paged-cache
+ * insert.
+ *
+ * Sources: the vLLM API pages of the Muse Spark specialized decode,
+ *   "...cutedsl.draft.context"       (ContextNorms, ContextKvStore and their kernels),
+ *   "...runtime.draft"               (ContextKV: _project, store),
+ *   "...cutedsl.common.draft_boundary" (boundary_fragments: the row-norm arithmetic).
+ *
+ * Conventions for every call:
+ *   - bf16 tensors are passed as uint16_t storage of the bf16 bit patterns.
+ *   - Every data pointer is caller-owned DEVICE memory unless stated otherwise.
+ *     The library never allocates, frees or reads device memory on the host.
+ *     Host pointer arrays (slots, caches) are read during the call only.
+ *   - `stream` is a hipStream_t (NULL: the null stream). Calls enqueue their
+ *     kernels on it and return without synchronising; nothing is kept after
+ *     the return.
+ *   - Return value: NRC_OK (0) or a negative errno-style code. All argument
+ *     checks finish before the first launch, so an error means nothing was
+ *     enqueued. nrc_last_error() then describes it.
+ *   - Results are deterministic: a call with the same inputs writes the same
+ *     bits.
+ *   - Outputs must not alias inputs.
+ */
+#ifndef NRC_H
+#define NRC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NRC_OK 0
+#define NRC_EIO (-5)       /* a HIP launch or runtime error */
+#define NRC_EINVAL (-22)   /* NULL where required, bad shape, stride or alignment */
+#define NRC_ENOTSUP (-95)  /* a shape the kernels do not take (hidden width, head dim, ...) */
+
+#define NRC_HIDDEN 8192               /* the norms' row width (one tile of the row norm) */
+#define NRC_HEAD_DIM 64               /* K/V head width */
+#define NRC_MAX_LAYERS_PER_LAUNCH 8   /* layers per store launch; more are split */
+
+/*
+ * nrc_context_norms - stack([pre_norm_l(hidden_norm(x)) for l]).
+ * Page "...cutedsl.draft.context", sections ContextNorms and
+ * _ContextNormsKernel; arithmetic of one norm per "...draft_boundary",
+ * boundary_fragments.
+ *
+ *   x          [T, D] bf16, contiguous, 16-byte aligned. D must be 8192.
+ *   hidden_w   [D] bf16, 16-byte aligned, or NULL for a weightless hidden norm.
+ *   pre_w      [L, D] bf16, contiguous, 16-byte aligned, or NULL (weightless
+ *              layer norms). Every layer norm shares pre_eps and pre_center.
+ *   hidden_eps, pre_eps        FP32 epsilons.
+ *   hidden_center, pre_center  gain centers: the weight used is w + center
+ *              (0.0 for a plain RMSNorm weight).
+ *   out        [L, T, D] bf16, contiguous, 16-byte aligned; element (l, t, c)
+ *              at (l * T + t) * D + c.
+ * Per row: S = sum of squares in the library's fixed order, r = 1/sqrt(S/D +
+ * eps) (one FMA, correctly rounded sqrt and divide), y = (x * r) * gamma,
+ * rounded to bf16. The hidden norm's bf16 output feeds the layer norms.
+ * T == 0 returns NRC_OK with nothing launched. Errors: NRC_EINVAL (NULL x or
+ * out with T > 0, T < 0, L < 1, misalignment), NRC_ENOTSUP (D != 8192).
+ */
+int32_t nrc_context_norms(const uint16_t* x, int64_t T, int64_t D, const uint16_t* hidden_w,
+                          const uint16_t* pre_w, int32_t L, float hidden_eps, float pre_eps,
+                          float hidden_center, float pre_center, uint16_t* out, void* stream);
+
+/*
+ * nrc_context_kv_project - the batched K/V projection C[l] = A[l] . B[l].
+ * Page "...runtime.draft", ContextKV._project (the bmm of the stacked layer
+ * norms against the stacked K/V weight).
+ *
+ *   normed  A: [L, T, D] bf16, contiguous, 16-byte aligned.
+ *   w       B: [L, D, N] bf16, contiguous, 16-byte aligned (the bmm's logical
+ *           right operand; N contiguous).
+ *   kv      C: [L, T, N] bf16, contiguous, 16-byte aligned; per row the H K
+ *           heads then the H V heads (N = 2 * H * 64).
+ * FP32 accumulation on the bf16 matrix cores, rounded to bf16 (nearest even)
+ * once. The summation order is the kernel's; results match an FP32 sum to
+ * bf16 tolerance. T == 0 returns NRC_OK. Errors: NRC_EINVAL (NULLs, L < 1,
+ * T < 0, misalignment), NRC_ENOTSUP (D not a positive multiple of 64, N not
+ * a positive multiple of 128).
+ */
+int32_t nrc_context_kv_project(const uint16_t* normed, const uint16_t* w, uint16_t* kv, int32_t L, int64_t T,
+                               int64_t D, int64_t N, void* stream);
+
+/*
+ * nrc_context_kv_store - weightless K-norm, GPT-J RoPE and paged-cache insert
+ * of L layers. Page "...cutedsl.draft.context", sections ContextKvStore,
+ * _ContextKvStoreKernel, _sum_squares_64 and _rope; operand checks per
+ * "...runtime.draft", ContextKV.store.
+ *
+ *   k, v       bf16 [L, T, H, 64] views: unit stride in the last dim, 64 between
+ *              heads; k_layer_stride, k_row_stride, v_layer_stride,
+ *              v_row_stride in elements (multiples of 8: 16-byte rows).
+ *              k and v 16-byte aligned. For the projection output [L, T, N]:
+ *              k = kv, v = kv + H * 64, layer stride T * N, row stride N.
+ *   positions  [>= rows] int64 device array; read only when cos_sin != NULL.
+ *   slots      HOST array of L device pointers, each int64 [rows], contiguous.
+ *              Row t of layer l goes to slot slots[l][t]; a negative slot skips
+ *              the row. Only rows 0 .. rows-1 are inserted (rows <= T).
+ *   cos_sin    [max_position, 64] bf16 (cos_0..31 then sin_0..31 per position),
+ *              contiguous, 16-byte aligned; NULL: no RoPE.
+ *   caches     HOST array of L device pointers, each a bf16 cache
+ *              [num_blocks, H, block_size, 128], contiguous, 16-byte aligned:
+ *              K of (slot, head h) at [slot / block_size, h, slot % block_size,
+ *              0:64], V at [..., 64:128].
+ *   eps        the K-norm's FP32 epsilon.
+ * Per (layer, row, head): S = the 64 squares folded by halves (strides 32 ..
+ * 1), r = 1/sqrt(S/64 + eps), n = bf16(k * r), then per pair (2j, 2j+1):
+ * (n0 c - n1 s, n1 c + n0 s) with one FMA each, rounded to bf16; V is copied
+ * bit for bit. No other cache cell is written.
+ * Preconditions (not checked: they need device reads): 0 <= positions[t] <
+ * max_position and 0 <= slot < num_blocks * block_size for inserted rows;
+ * non-negative slots distinct within a layer. A row that breaks the range
+ * preconditions is skipped by the kernel (never written out of bounds).
+ * rows == 0 returns NRC_OK. Layers beyond 8 take further launches.
+ * Errors: NRC_EINVAL (NULLs, rows > T, misaligned strides or pointers, H < 1),
+ * NRC_ENOTSUP (H not a power of two, num_blocks * block_size >= 2^31).
+ */
+int32_t nrc_context_kv_store(const uint16_t* k, const uint16_t* v, int64_t k_layer_stride, int64_t k_row_stride,
+                             int64_t v_layer_stride, int64_t v_row_stride, const int64_t* positions,
+                             const int64_t* const* slots, int64_t rows, int64_t T, const uint16_t* cos_sin,
+                             int64_t max_position, uint16_t* const* caches, int64_t num_blocks, int64_t block_size,
+                             int32_t H, int32_t L, float eps, void* stream);
+
+/* Thread-local description of the last non-zero status of this thread. */
+const char* nrc_last_error(void);
+
+/* ABI version: 1. */
+int32_t nrc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NRC_H */

@@ -1,0 +1,217 @@
+"""ctypes view of the CPU oracle (oracle/oracle.c) over numpy arrays.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+bench's cpu_baseline leg. The product package never imports it, and it
+imports nothing from the product package. bf16 tensors are numpy uint16
+arrays holding the bf16 bit patterns.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.environ.get("NRC_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+D = 8192
+HEAD_DIM = 64
+
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_f32 = ctypes.c_float
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _build
+
+            _build.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.nrc_oracle_bf16.argtypes = [_f32]
+        L.nrc_oracle_bf16.restype = ctypes.c_uint16
+        L.nrc_oracle_rs.argtypes = [_f32]
+        L.nrc_oracle_rs.restype = _f32
+        L.nrc_oracle_bf16_array.argtypes = [_f32p, _u16p, _i64]
+        L.nrc_oracle_bf16_array.restype = None
+        L.nrc_oracle_rs_array.argtypes = [_f32p, _f32p, _i64]
+        L.nrc_oracle_rs_array.restype = None
+        L.nrc_oracle_sumsq_row.argtypes = [_f32p]
+        L.nrc_oracle_sumsq_row.restype = _f32
+        L.nrc_oracle_sumsq_head.argtypes = [_f32p]
+        L.nrc_oracle_sumsq_head.restype = _f32
+        L.nrc_oracle_context_norms.argtypes = [_u16p, _i64, _i64, _u16p, _u16p, _i32, _f32, _f32, _f32, _f32, _u16p]
+        L.nrc_oracle_context_norms.restype = _i32
+        L.nrc_oracle_kv_project.argtypes = [_u16p, _u16p, _f32p, _i32, _i64, _i64, _i64]
+        L.nrc_oracle_kv_project.restype = _i32
+        L.nrc_oracle_knorm_rope_head.argtypes = [_u16p, _u16p, _f32, _u16p]
+        L.nrc_oracle_knorm_rope_head.restype = None
+        L.nrc_oracle_cache_offset.argtypes = [_i64, _i64, _i32, _i32]
+        L.nrc_oracle_cache_offset.restype = _i64
+        L.nrc_oracle_context_kv_store.argtypes = [
+            _u16p, _i32, _i64, _i32, _i64p, _i64p, _i64, _u16p, _i64, _u16p, _i64, _i64, _f32]
+        L.nrc_oracle_context_kv_store.restype = _i32
+        L.nrc_oracle_chain.argtypes = [
+            _u16p, _i64, _u16p, _u16p, _i32, _f32, _f32, _u16p, _i32, _i64p, _i64p, _i64, _u16p, _i64,
+            _u16p, _i64, _i64, _f32, _u16p, _u16p]
+        L.nrc_oracle_chain.restype = _i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a, ctype):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == dtype, (a.dtype, dtype)
+    return a
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(st, what):
+    if st != 0:
+        raise OracleError(f"{what}: oracle precondition failed ({st})")
+
+
+# ------------------------------------------------------------------ scalars
+
+def bf16(x):
+    """f32 -> bf16 bits (round to nearest even; NaN -> 0x7FC0), elementwise."""
+    shape = np.shape(x)
+    x = _c(np.asarray(x, dtype=np.float32), np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().nrc_oracle_bf16_array(_ptr(x, ctypes.c_float), _ptr(out, ctypes.c_uint16), x.size)
+    return out.reshape(shape)
+
+
+def rs(v):
+    """1 / sqrt(v), both correctly rounded in FP32, elementwise."""
+    shape = np.shape(v)
+    v = _c(np.asarray(v, dtype=np.float32), np.float32)
+    out = np.empty(v.shape, dtype=np.float32)
+    lib().nrc_oracle_rs_array(_ptr(v, ctypes.c_float), _ptr(out, ctypes.c_float), v.size)
+    return out.reshape(shape)
+
+
+def sumsq_row(u):
+    u = _c(np.asarray(u, dtype=np.float32), np.float32)
+    assert u.shape == (D,)
+    return np.float32(lib().nrc_oracle_sumsq_row(_ptr(u, ctypes.c_float)))
+
+
+def sumsq_head(k):
+    k = _c(np.asarray(k, dtype=np.float32), np.float32)
+    assert k.shape == (HEAD_DIM,)
+    return np.float32(lib().nrc_oracle_sumsq_head(_ptr(k, ctypes.c_float)))
+
+
+# ------------------------------------------------------------------- chain
+
+def context_norms(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hidden_center=0.0, pre_center=0.0):
+    """x [T, 8192] bf16 bits -> [L, T, 8192] bf16 bits."""
+    x = _c(x, np.uint16)
+    T = x.shape[0]
+    assert x.shape == (T, D)
+    hw = None if hidden_w is None else _c(hidden_w, np.uint16)
+    pw = None if pre_w is None else _c(pre_w, np.uint16)
+    if hw is not None:
+        assert hw.shape == (D,)
+    if pw is not None:
+        assert pw.shape == (L, D)
+    out = np.empty((L, T, D), dtype=np.uint16)
+    st = lib().nrc_oracle_context_norms(
+        _ptr(x, ctypes.c_uint16), T, D, _ptr(hw, ctypes.c_uint16), _ptr(pw, ctypes.c_uint16), L,
+        hidden_eps, pre_eps, hidden_center, pre_center, _ptr(out, ctypes.c_uint16))
+    _check(st, "context_norms")
+    return out
+
+
+def kv_project(A, B):
+    """A [L, T, D] bf16 bits, B [L, D, N] bf16 bits -> C [L, T, N] float32."""
+    A = _c(A, np.uint16)
+    B = _c(B, np.uint16)
+    L, T, Dd = A.shape
+    assert B.shape[0] == L and B.shape[1] == Dd
+    N = B.shape[2]
+    C = np.empty((L, T, N), dtype=np.float32)
+    st = lib().nrc_oracle_kv_project(_ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16), _ptr(C, ctypes.c_float),
+                                     L, T, Dd, N)
+    _check(st, "kv_project")
+    return C
+
+
+def knorm_rope_head(k, cs_row, eps=1e-6):
+    k = _c(k, np.uint16)
+    assert k.shape == (HEAD_DIM,)
+    cs = None if cs_row is None else _c(cs_row, np.uint16)
+    out = np.empty(HEAD_DIM, dtype=np.uint16)
+    lib().nrc_oracle_knorm_rope_head(_ptr(k, ctypes.c_uint16), _ptr(cs, ctypes.c_uint16), eps,
+                                     _ptr(out, ctypes.c_uint16))
+    return out
+
+
+def cache_offset(slot, block_size, H, h):
+    return int(lib().nrc_oracle_cache_offset(int(slot), int(block_size), int(H), int(h)))
+
+
+def context_kv_store(kv, H, positions, slots, cos_sin, caches, block_size, eps=1e-6):
+    """In place on `caches` [L, num_blocks, H, block_size, 128] bf16 bits.
+
+    kv [L, T, 2 H 64] bf16 bits; positions [T] int64; slots [L, rows] int64;
+    cos_sin [max_position, 64] bf16 bits or None."""
+    kv = _c(kv, np.uint16)
+    L, T, N = kv.shape
+    assert N == 2 * H * HEAD_DIM
+    positions = _c(positions, np.int64)
+    slots = _c(slots, np.int64)
+    assert slots.ndim == 2 and slots.shape[0] == L
+    rows = slots.shape[1]
+    assert caches.flags.c_contiguous and caches.dtype == np.uint16
+    num_blocks = caches.shape[1]
+    assert caches.shape == (L, num_blocks, H, block_size, 2 * HEAD_DIM)
+    cs = None if cos_sin is None else _c(cos_sin, np.uint16)
+    max_pos = 0 if cs is None else cs.shape[0]
+    st = lib().nrc_oracle_context_kv_store(
+        _ptr(kv, ctypes.c_uint16), L, T, H, _ptr(positions, ctypes.c_int64), _ptr(slots, ctypes.c_int64), rows,
+        _ptr(cs, ctypes.c_uint16), max_pos, _ptr(caches, ctypes.c_uint16), num_blocks, block_size, eps)
+    _check(st, "context_kv_store")
+
+
+def chain(x, hidden_w, pre_w, L, w_kv, H, positions, slots, cos_sin, caches, block_size,
+          hidden_eps=1e-6, pre_eps=1e-6, k_eps=1e-6):
+    """The whole chain on the CPU; caches updated in place. Returns (normed, kv)."""
+    x = _c(x, np.uint16)
+    T = x.shape[0]
+    N = 2 * H * HEAD_DIM
+    w_kv = _c(w_kv, np.uint16)
+    assert w_kv.shape == (L, D, N)
+    hw = None if hidden_w is None else _c(hidden_w, np.uint16)
+    pw = None if pre_w is None else _c(pre_w, np.uint16)
+    positions = _c(positions, np.int64)
+    slots = _c(slots, np.int64)
+    rows = slots.shape[1]
+    num_blocks = caches.shape[1]
+    cs = None if cos_sin is None else _c(cos_sin, np.uint16)
+    max_pos = 0 if cs is None else cs.shape[0]
+    normed = np.empty((L, T, D), dtype=np.uint16)
+    kv = np.empty((L, T, N), dtype=np.uint16)
+    st = lib().nrc_oracle_chain(
+        _ptr(x, ctypes.c_uint16), T, _ptr(hw, ctypes.c_uint16), _ptr(pw, ctypes.c_uint16), L, hidden_eps, pre_eps,
+        _ptr(w_kv, ctypes.c_uint16), H, _ptr(positions, ctypes.c_int64), _ptr(slots, ctypes.c_int64), rows,
+        _ptr(cs, ctypes.c_uint16), max_pos, _ptr(caches, ctypes.c_uint16), num_blocks, block_size, k_eps,
+        _ptr(normed, ctypes.c_uint16), _ptr(kv, ctypes.c_uint16))
+    _check(st, "chain")
+    return normed, kv
