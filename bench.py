@@ -1,0 +1,239 @@
+"""Throughput of the context K/V chain on one MI355X.
+
+One step = the whole hot path over one batch of synthetic context rows:
+context_norms -> context_kv_project -> context_kv_store (all three kernels,
+on one stream, inputs and outputs resident in HBM). The default workload is
+the long-context configuration (L=4 draft layers, T=16384 rows, D=8192,
+H=8 KV heads, RoPE table [131072, 64], block size 16, 8192 blocks).
+
+    python bench.py [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
+
+Prints ONE JSON line on stdout; progress goes to stderr. Per-kernel launch
+durations come from HIP events recorded on the stream the kernels run on
+(torch's current stream, which the binding passes to every call).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg, slots_np):
+    """Per-launch algorithmic HBM bytes of the norms and the store.
+
+    norms: read x once (2 D per row), write L rows (2 L D per row), plus the
+           weights once ((1 + L) 2 D, or none when weightless).
+    store: 8 B of slot per (layer, row); per inserted (layer, row): 8 B of
+           position + 128 B of cos/sin with RoPE, K and V read (2 N) and
+           written (2 N). Rows with a negative slot read nothing else."""
+    import numpy as np
+
+    D, L, T, N = 8192, cfg.L, cfg.T, cfg.N
+    w = (1 if cfg.hidden_weighted else 0) * 2 * D + (L if cfg.pre_weighted else 0) * 2 * D
+    norms = T * (2 * D + 2 * L * D) + w
+    valid = int((slots_np >= 0).sum())  # over all layers
+    store = 8 * L * T + valid * (2 * N + 2 * N + ((8 + 128) if cfg.rope else 0))
+    flops = 2 * L * T * D * N
+    return norms, store, flops
+
+
+def traffic_from_profiles(kernel_tag):
+    """HBM bytes per launch measured with rocprofv3 counters, if a committed
+    summary for the current kernel source exists (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_tag)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    from norm_rope_cache_amd import build
+
+    if rec.get("source_hash") != build.source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(d, cfg, rows):
+    """The CPU oracle as it stands (single thread), on the first `rows` rows
+    of the workload: norms, projection, store. Returns rows/s."""
+    import numpy as np
+
+    import oracle
+
+    x = np.ascontiguousarray(d["x"][:rows])
+    pos = d["positions"][:rows]
+    slots = np.ascontiguousarray(d["slots"][:, :rows])
+    caches = d["caches_host_sample"]
+    t0 = time.perf_counter()
+    oracle.chain(x, d["hidden_w"], d["pre_w"], cfg.L, d["w_kv"], cfg.H, pos, slots, d["cos_sin"], caches,
+                 cfg.block_size)
+    dt = time.perf_counter() - t0
+    return rows / dt, dt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} / WORLD_SIZE {world} is not supported "
+              "(the chain needs no exchange between GPUs; see the design notes on sharding)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import norm_rope_cache_amd as nrc
+    from norm_rope_cache_amd import synth
+
+    cfg = synth.CONFIGS[args.workload]
+    log(f"generating {cfg.name}: L={cfg.L} T={cfg.T} H={cfg.H}")
+    d = synth.make_inputs(cfg, with_cache=False)
+    dev = torch.device("cuda", 0)
+
+    def dv(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    x = dv(d["x"])
+    hw = None if d["hidden_w"] is None else dv(d["hidden_w"])
+    pw = None if d["pre_w"] is None else dv(d["pre_w"])
+    w_kv = dv(d["w_kv"])
+    cos_sin = None if d["cos_sin"] is None else dv(d["cos_sin"])
+    positions = dv(d["positions"])
+    slots = dv(d["slots"])
+    caches = torch.empty((cfg.L, cfg.num_blocks, cfg.H, cfg.block_size, 128), dtype=torch.bfloat16, device=dev)
+    caches.view(torch.int16).random_(-32768, 32767)
+    normed = torch.empty((cfg.L, cfg.T, 8192), dtype=torch.bfloat16, device=dev)
+    kv = torch.empty((cfg.L, cfg.T, cfg.N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        nrc.context_norms(x, hw, pw, cfg.L, d["hidden_eps"], d["pre_eps"], out=normed)
+        if ev:
+            ev[1].record()
+        nrc.context_kv_project(normed, w_kv, out=kv)
+        if ev:
+            ev[2].record()
+        nrc.context_kv_store(kv, positions, slots, cos_sin, caches, cfg.H, d["k_eps"])
+        if ev:
+            ev[3].record()
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    k_ms = {"context_norms": [], "context_kv_project": [], "context_kv_store": []}
+    for ev in events:
+        k_ms["context_norms"].append(ev[0].elapsed_time(ev[1]))
+        k_ms["context_kv_project"].append(ev[1].elapsed_time(ev[2]))
+        k_ms["context_kv_store"].append(ev[2].elapsed_time(ev[3]))
+    avg = {k: sum(v) / len(v) for k, v in k_ms.items()}
+    log("per-kernel ms: " + ", ".join(f"{k}={v:.4f}" for k, v in avg.items()) + f"; wall/step {ms_step:.4f}")
+
+    norms_b, store_b, flops = algorithmic_bytes(cfg, d["slots"])
+    kernels = {
+        "context_norms": {"bound": "hbm", "ms": avg["context_norms"], "bytes": norms_b,
+                          "achieved_GBs": norms_b / (avg["context_norms"] * 1e-3) / 1e9},
+        "context_kv_project": {"bound": "mfma", "ms": avg["context_kv_project"], "flops": flops,
+                               "achieved_TFLOPs": flops / (avg["context_kv_project"] * 1e-3) / 1e12},
+        "context_kv_store": {"bound": "hbm", "ms": avg["context_kv_store"], "bytes": store_b,
+                             "achieved_GBs": store_b / (avg["context_kv_store"] * 1e-3) / 1e9},
+    }
+    for k, rec in kernels.items():
+        if rec["bound"] == "hbm":
+            rec["frac"] = rec["achieved_GBs"] / HBM_PEAK_GBS
+        else:
+            rec["frac"] = rec["achieved_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS
+        rec["traffic_bytes"] = traffic_from_profiles(k)
+
+    # the dominant kernel (longest launch) carries the roofline object
+    dom = max(avg, key=avg.get)
+    rd = kernels[dom]
+    if rd["bound"] == "mfma":
+        roofline = {"bound": "mfma", "achieved": rd["achieved_TFLOPs"], "peak": BF16_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": rd["frac"], "traffic": rd["traffic_bytes"], "kernel": dom}
+    else:
+        roofline = {"bound": "hbm", "achieved": rd["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": rd["frac"], "traffic": rd["traffic_bytes"], "kernel": dom}
+
+    rows_per_s = cfg.T * args.steps / wall
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        rows = min(args.cpu_rows, cfg.T)
+        d["caches_host_sample"] = synth.random_bits_u16(cfg.stream(synth.TID_CACHE),
+                                                       (cfg.L, cfg.num_blocks, cfg.H, cfg.block_size, 128))
+        log(f"cpu baseline: oracle chain on {rows} rows")
+        v, dt = cpu_baseline(d, cfg, rows)
+        cpu = {"value": v, "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {rows} of {cfg.T} rows of the {cfg.name} workload, whole chain "
+                         f"(norms, FP32 projection, store), single-threaded plain C, {dt:.1f} s"}
+
+    out = {
+        "metric": "context rows/s (T=16K, L=4, D=8192); % HBM BW peak; bmm % MFMA peak",
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: L={cfg.L} T={cfg.T} D=8192 H={cfg.H} N={cfg.N} "
+                        f"block_size={cfg.block_size} num_blocks={cfg.num_blocks} "
+                        f"rope={'[%d,64]' % cfg.max_position if cfg.rope else 'off'}",
+            "global_batch": cfg.T,
+            "seq_len": cfg.T,
+            "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

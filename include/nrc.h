@@ -126,6 +126,16 @@ int32_t nrc_context_kv_store(const uint16_t* k, const uint16_t* v, int64_t k_lay
                              int64_t max_position, uint16_t* const* caches, int64_t num_blocks, int64_t block_size,
                              int32_t H, int32_t L, float eps, void* stream);
 
+/*
+ * nrc_check_scalars - diagnostic: the device primitives every kernel uses,
+ * applied elementwise to n FP32 values (device arrays), so that they can be
+ * compared with a reference over all 2^32 inputs:
+ *   bf16_out[i]  = f32 -> bf16 rounding of in[i] (nearest even; NaN -> 0x7FC0)
+ *   rsqrt_out[i] = 1 / sqrt(in[i]), both correctly rounded
+ * Either output may be NULL. n <= 2^32. Errors: NRC_EINVAL.
+ */
+int32_t nrc_check_scalars(const float* in, uint16_t* bf16_out, float* rsqrt_out, int64_t n, void* stream);
+
 /* Thread-local description of the last non-zero status of this thread. */
 const char* nrc_last_error(void);
 

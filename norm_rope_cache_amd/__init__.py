@@ -1,0 +1,247 @@
+"""norm_rope_cache_amd: the DSpark draft's context K/V chain on MI355X (gfx950).
+
+A thin ctypes binding over libnrc.so (include/nrc.h). Each function checks
+torch tensor dtypes/shapes, passes raw device pointers and the current HIP
+stream, and raises NrcError on a non-zero status. Every step of the chain
+runs in the library's HIP kernels; there is no CPU or PyTorch fallback: if
+libnrc.so is missing, every call raises.
+
+    context_norms(x, hidden_w, pre_w, L, ...)      -> [L, T, 8192] bf16
+    context_kv_project(normed, w_kv)               -> [L, T, N] bf16
+    context_kv_store(kv, positions, slots, cos_sin, caches, H, ...)   (in place)
+    context_kv_chain(...)                          all three in order
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "NrcError",
+    "context_norms",
+    "context_kv_project",
+    "context_kv_store",
+    "context_kv_chain",
+    "kv_views",
+    "check_scalars",
+    "library_path",
+    "abi_version",
+]
+
+HIDDEN = 8192
+HEAD_DIM = 64
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libnrc.so")
+_lib = None
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_f32 = ctypes.c_float
+
+
+class NrcError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"libnrc status {code}: {message}")
+        self.code = code
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"libnrc.so not built at {_LIB_PATH}: run `python -m norm_rope_cache_amd.build` "
+            "(there is no fallback path)")
+    L = ctypes.CDLL(_LIB_PATH)
+    L.nrc_last_error.restype = ctypes.c_char_p
+    L.nrc_last_error.argtypes = []
+    L.nrc_abi_version.restype = _i32
+    L.nrc_abi_version.argtypes = []
+    L.nrc_context_norms.restype = _i32
+    L.nrc_context_norms.argtypes = [_vp, _i64, _i64, _vp, _vp, _i32, _f32, _f32, _f32, _f32, _vp, _vp]
+    L.nrc_context_kv_project.restype = _i32
+    L.nrc_context_kv_project.argtypes = [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp]
+    L.nrc_context_kv_store.restype = _i32
+    L.nrc_context_kv_store.argtypes = [
+        _vp, _vp, _i64, _i64, _i64, _i64, _vp, ctypes.POINTER(_vp), _i64, _i64, _vp, _i64,
+        ctypes.POINTER(_vp), _i64, _i64, _i32, _i32, _f32, _vp]
+    L.nrc_check_scalars.restype = _i32
+    L.nrc_check_scalars.argtypes = [_vp, _vp, _vp, _i64, _vp]
+    _lib = L
+    return L
+
+
+def abi_version():
+    return int(_load().nrc_abi_version())
+
+
+def _check(code):
+    if code != 0:
+        msg = _load().nrc_last_error().decode(errors="replace")
+        raise NrcError(code, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _bf16(t, name, contiguous=True):
+    import torch
+
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, not {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def context_norms(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hidden_center=0.0, pre_center=0.0,
+                  out=None, stream=None):
+    """stack([pre_norm_l(hidden_norm(x)) for l]): x [T, 8192] bf16 ->
+    [L, T, 8192] bf16 (written into `out` when given)."""
+    import torch
+
+    _bf16(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [T, 8192]")
+    T, D = x.shape
+    if hidden_w is not None:
+        _bf16(hidden_w, "hidden_w")
+        if tuple(hidden_w.shape) != (D,):
+            raise ValueError("hidden_w must be [D]")
+    if pre_w is not None:
+        _bf16(pre_w, "pre_w")
+        if tuple(pre_w.shape) != (L, D):
+            raise ValueError("pre_w must be [L, D]")
+    if out is None:
+        out = torch.empty((L, T, D), dtype=torch.bfloat16, device=x.device)
+    else:
+        _bf16(out, "out")
+        if tuple(out.shape) != (L, T, D):
+            raise ValueError("out must be [L, T, D]")
+    _check(_load().nrc_context_norms(_ptr(x), T, D, _ptr(hidden_w), _ptr(pre_w), L, hidden_eps, pre_eps,
+                                     hidden_center, pre_center, _ptr(out), _stream(stream)))
+    return out
+
+
+def context_kv_project(normed, w_kv, out=None, stream=None):
+    """[L, T, D] x [L, D, N] -> [L, T, N] bf16 (FP32 accumulation)."""
+    import torch
+
+    _bf16(normed, "normed")
+    _bf16(w_kv, "w_kv")
+    L, T, D = normed.shape
+    if w_kv.dim() != 3 or w_kv.shape[0] != L or w_kv.shape[1] != D:
+        raise ValueError("w_kv must be [L, D, N]")
+    N = w_kv.shape[2]
+    if out is None:
+        out = torch.empty((L, T, N), dtype=torch.bfloat16, device=normed.device)
+    else:
+        _bf16(out, "out")
+        if tuple(out.shape) != (L, T, N):
+            raise ValueError("out must be [L, T, N]")
+    _check(_load().nrc_context_kv_project(_ptr(normed), _ptr(w_kv), _ptr(out), L, T, D, N, _stream(stream)))
+    return out
+
+
+def kv_views(kv, H):
+    """k, v views [L, T, H, 64] of a projection output [L, T, 2 H 64]."""
+    L, T, N = kv.shape
+    v5 = kv.view(L, T, 2, H, HEAD_DIM)
+    return v5[:, :, 0], v5[:, :, 1]
+
+
+def context_kv_store(kv, positions, slots, cos_sin, caches, H, eps=1e-6, rows=None, k=None, v=None,
+                     stream=None):
+    """K-norm + GPT-J RoPE + paged insert, in place on `caches`.
+
+    kv       [L, T, 2 H 64] bf16 projection output (or pass k, v views
+             [L, T, H, 64] with unit last stride and head stride 64)
+    positions [T] int64 (unused without cos_sin)
+    slots    [L, rows] int64 tensor or a list of L [rows] int64 tensors
+    cos_sin  [max_position, 64] bf16 or None (RoPE off)
+    caches   [L, num_blocks, H, block_size, 128] bf16 tensor or a list of L
+             [num_blocks, H, block_size, 128] tensors
+    """
+    import torch
+
+    if k is None:
+        _bf16(kv, "kv")
+        k, v = kv_views(kv, H)
+    for name, t in (("k", k), ("v", v)):
+        _bf16(t, name, contiguous=False)
+        if t.dim() != 4 or t.shape[2] != H or t.shape[3] != HEAD_DIM or t.stride(3) != 1 or t.stride(2) != HEAD_DIM:
+            raise ValueError(f"{name} must be an [L, T, H, 64] view with unit last stride and head stride 64")
+    L, T = k.shape[0], k.shape[1]
+    cache_list = list(caches) if not isinstance(caches, torch.Tensor) else [caches[i] for i in range(caches.shape[0])]
+    slot_list = list(slots) if not isinstance(slots, torch.Tensor) else [slots[i] for i in range(slots.shape[0])]
+    if len(cache_list) != L or len(slot_list) != L:
+        raise ValueError("one cache and one slot mapping per layer")
+    c0 = cache_list[0]
+    if c0.dim() != 4 or c0.shape[1] != H or c0.shape[3] != 2 * HEAD_DIM:
+        raise ValueError("caches must be [num_blocks, H, block_size, 128]")
+    nb, _, bs, _ = c0.shape
+    for c in cache_list:
+        _bf16(c, "cache")
+        if c.shape != c0.shape:
+            raise ValueError("all caches must have one shape")
+    n_rows = slot_list[0].shape[0] if rows is None else rows
+    for s in slot_list:
+        if s.dtype != torch.int64 or s.dim() != 1 or not s.is_contiguous() or s.shape[0] != slot_list[0].shape[0]:
+            raise ValueError("slots must be contiguous int64 [rows] tensors of one length")
+    if cos_sin is not None:
+        _bf16(cos_sin, "cos_sin")
+        if cos_sin.dim() != 2 or cos_sin.shape[1] != HEAD_DIM:
+            raise ValueError("cos_sin must be [max_position, 64]")
+        if positions is None or positions.dtype != torch.int64 or not positions.is_contiguous():
+            raise ValueError("positions must be a contiguous int64 tensor")
+        if positions.shape[0] < n_rows:
+            raise ValueError("positions shorter than the inserted rows")
+    slot_arr = (_vp * L)(*[s.data_ptr() for s in slot_list])
+    cache_arr = (_vp * L)(*[c.data_ptr() for c in cache_list])
+    max_pos = 0 if cos_sin is None else cos_sin.shape[0]
+    _check(_load().nrc_context_kv_store(
+        _ptr(k), _ptr(v), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
+        _ptr(positions) if cos_sin is not None else None, slot_arr, n_rows, T, _ptr(cos_sin), max_pos, cache_arr,
+        nb, bs, H, L, eps, _stream(stream)))
+
+
+def check_scalars(x, want_bf16=True, want_rsqrt=True, stream=None):
+    """Diagnostic: the library's device bf16 rounding and 1/sqrt applied to
+    a float32 GPU tensor; returns (bf16 bits as int16 tensor, float32 tensor)."""
+    import torch
+
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float32 GPU tensor")
+    bf = torch.empty(x.shape, dtype=torch.int16, device=x.device) if want_bf16 else None
+    rs = torch.empty_like(x) if want_rsqrt else None
+    _check(_load().nrc_check_scalars(_ptr(x), _ptr(bf), _ptr(rs), x.numel(), _stream(stream)))
+    return bf, rs
+
+
+def context_kv_chain(x, hidden_w, pre_w, w_kv, positions, slots, cos_sin, caches, H, hidden_eps=1e-6,
+                     pre_eps=1e-6, k_eps=1e-6, normed=None, kv=None, stream=None):
+    """The whole chain: norms -> projection -> K-norm/RoPE/insert. `normed`
+    [L, T, 8192] and `kv` [L, T, N] may be passed in as preallocated
+    intermediates. Returns (normed, kv)."""
+    L = w_kv.shape[0]
+    normed = context_norms(x, hidden_w, pre_w, L, hidden_eps, pre_eps, out=normed, stream=stream)
+    kv = context_kv_project(normed, w_kv, out=kv, stream=stream)
+    context_kv_store(kv, positions, slots, cos_sin, caches, H, k_eps, stream=stream)
+    return normed, kv

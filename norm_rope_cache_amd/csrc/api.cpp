@@ -1,0 +1,185 @@
+// The C ABI of libnrc (include/nrc.h): argument checks, then launches.
+//
+// Every check runs on the host before the first launch, so a non-zero status
+// means nothing was enqueued; nrc_last_error() describes it. The operand
+// rules follow the vLLM pages: ContextNorms (8192-wide rows, T >= 1 rows;
+// zero rows are a no-op here), ContextKV.store (bf16 caches with 64-wide
+// heads, even strides, 4-byte alignment, fewer than 2^31 slots, slot
+// mappings of one length), ContextKvStore (rows == 0 is a no-op; at most 8
+// layers per launch) and the runtime page's eligibility rules (head dim 64,
+// KV heads a power of two).
+#include <errno.h>
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/nrc.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int num_cus() {
+    static int cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+int launch_status(int rc, const char* what) {
+    if (rc != 0) {
+        hipError_t e = hipGetLastError();
+        return fail(NRC_EIO, "%s: launch failed (%s)", what, hipGetErrorString(e));
+    }
+    return NRC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nrc_last_error(void) { return g_err; }
+
+int32_t nrc_abi_version(void) { return 1; }
+
+int32_t nrc_context_norms(const uint16_t* x, int64_t T, int64_t D, const uint16_t* hidden_w, const uint16_t* pre_w,
+                          int32_t L, float hidden_eps, float pre_eps, float hidden_center, float pre_center,
+                          uint16_t* out, void* stream) {
+    if (D != NRC_HIDDEN) return fail(NRC_ENOTSUP, "context_norms: rows of %lld, not %d", (long long)D, NRC_HIDDEN);
+    if (T < 0) return fail(NRC_EINVAL, "context_norms: T = %lld < 0", (long long)T);
+    if (L < 1) return fail(NRC_EINVAL, "context_norms: L = %d < 1", L);
+    if (T > ((int64_t)1 << 40) / ((int64_t)L * D))
+        return fail(NRC_EINVAL, "context_norms: output of %lld x %d rows too large", (long long)T, L);
+    if (T == 0) return NRC_OK;
+    if (!x || !out) return fail(NRC_EINVAL, "context_norms: NULL x or out");
+    if (!aligned(x, 16) || !aligned(out, 16) || (hidden_w && !aligned(hidden_w, 16)) ||
+        (pre_w && !aligned(pre_w, 16)))
+        return fail(NRC_EINVAL, "context_norms: operands must be 16-byte aligned");
+    nrc::NormsArgs a{x, T, hidden_w, pre_w, L, hidden_eps, pre_eps, hidden_center, pre_center, out, num_cus()};
+    return launch_status(nrc::launch_context_norms(a, (hipStream_t)stream), "context_norms");
+}
+
+int32_t nrc_context_kv_project(const uint16_t* normed, const uint16_t* w, uint16_t* kv, int32_t L, int64_t T,
+                               int64_t D, int64_t N, void* stream) {
+    if (L < 1) return fail(NRC_EINVAL, "context_kv_project: L = %d < 1", L);
+    if (T < 0) return fail(NRC_EINVAL, "context_kv_project: T = %lld < 0", (long long)T);
+    if (D <= 0 || D % 64) return fail(NRC_ENOTSUP, "context_kv_project: D = %lld is not a positive multiple of 64",
+                                      (long long)D);
+    if (N <= 0 || N % 128)
+        return fail(NRC_ENOTSUP, "context_kv_project: N = %lld is not a positive multiple of 128 (2 H 64)",
+                    (long long)N);
+    if (T > ((int64_t)1 << 31) || D > ((int64_t)1 << 20) || N > ((int64_t)1 << 20) ||
+        (int64_t)L * ((T + 127) / 128) * (N / 128) > ((int64_t)1 << 30))
+        return fail(NRC_EINVAL, "context_kv_project: shape too large");
+    if (T == 0) return NRC_OK;
+    if (!normed || !w || !kv) return fail(NRC_EINVAL, "context_kv_project: NULL operand");
+    if (!aligned(normed, 16) || !aligned(w, 16) || !aligned(kv, 16))
+        return fail(NRC_EINVAL, "context_kv_project: operands must be 16-byte aligned");
+    nrc::ProjectArgs a{normed, w, kv, L, T, D, N, num_cus()};
+    return launch_status(nrc::launch_kv_project(a, (hipStream_t)stream), "context_kv_project");
+}
+
+int32_t nrc_context_kv_store(const uint16_t* k, const uint16_t* v, int64_t k_layer_stride, int64_t k_row_stride,
+                             int64_t v_layer_stride, int64_t v_row_stride, const int64_t* positions,
+                             const int64_t* const* slots, int64_t rows, int64_t T, const uint16_t* cos_sin,
+                             int64_t max_position, uint16_t* const* caches, int64_t num_blocks, int64_t block_size,
+                             int32_t H, int32_t L, float eps, void* stream) {
+    if (L < 1) return fail(NRC_EINVAL, "context_kv_store: L = %d < 1", L);
+    if (H < 1) return fail(NRC_EINVAL, "context_kv_store: H = %d < 1", H);
+    if (H & (H - 1)) return fail(NRC_ENOTSUP, "context_kv_store: %d KV heads, not a power of two", H);
+    if (T < 0 || rows < 0 || rows > T)
+        return fail(NRC_EINVAL, "context_kv_store: rows = %lld must lie in [0, T = %lld]", (long long)rows,
+                    (long long)T);
+    if (num_blocks < 1 || block_size < 1)
+        return fail(NRC_EINVAL, "context_kv_store: num_blocks and block_size must be >= 1");
+    if (num_blocks > (((int64_t)1 << 31) - 1) / block_size)
+        return fail(NRC_ENOTSUP, "context_kv_store: %lld x %lld slots do not fit 31 bits", (long long)num_blocks,
+                    (long long)block_size);
+    if (rows * H > ((int64_t)1 << 25))
+        return fail(NRC_ENOTSUP, "context_kv_store: rows x heads = %lld too large for one call",
+                    (long long)(rows * H));
+    if (rows == 0) return NRC_OK;
+    if (!k || !v || !slots || !caches) return fail(NRC_EINVAL, "context_kv_store: NULL operand");
+    if (!aligned(k, 16) || !aligned(v, 16))
+        return fail(NRC_EINVAL, "context_kv_store: k and v must be 16-byte aligned");
+    if ((k_layer_stride | k_row_stride | v_layer_stride | v_row_stride) & 7)
+        return fail(NRC_EINVAL, "context_kv_store: k/v strides must be multiples of 8 elements");
+    if (k_layer_stride < 0 || k_row_stride < 0 || v_layer_stride < 0 || v_row_stride < 0)
+        return fail(NRC_EINVAL, "context_kv_store: negative stride");
+    if (cos_sin) {
+        if (!positions) return fail(NRC_EINVAL, "context_kv_store: RoPE needs positions");
+        if (max_position < 1) return fail(NRC_EINVAL, "context_kv_store: max_position < 1");
+        if (!aligned(cos_sin, 16) || !aligned(positions, 8))
+            return fail(NRC_EINVAL, "context_kv_store: cos_sin must be 16-byte, positions 8-byte aligned");
+    }
+    for (int32_t l = 0; l < L; ++l) {
+        if (!slots[l] || !caches[l]) return fail(NRC_EINVAL, "context_kv_store: NULL slots or cache of layer %d", l);
+        if (!aligned(slots[l], 8) || !aligned(caches[l], 16))
+            return fail(NRC_EINVAL, "context_kv_store: layer %d: slots must be 8-byte, cache 16-byte aligned", l);
+    }
+
+    const uint32_t bs = (uint32_t)block_size;
+    int32_t bs_shift = -1;
+    if ((bs & (bs - 1)) == 0) {
+        bs_shift = 0;
+        while ((1u << bs_shift) != bs) ++bs_shift;
+    }
+    uint32_t log2H = 0;
+    while ((1u << log2H) != (uint32_t)H) ++log2H;
+
+    for (int32_t first = 0; first < L; first += NRC_MAX_LAYERS_PER_LAUNCH) {
+        const int32_t n = L - first < NRC_MAX_LAYERS_PER_LAUNCH ? L - first : NRC_MAX_LAYERS_PER_LAUNCH;
+        nrc::KvStoreArgs a{};
+        a.k = k + first * k_layer_stride;
+        a.v = v + first * v_layer_stride;
+        a.k_ls = k_layer_stride;
+        a.k_rs = k_row_stride;
+        a.v_ls = v_layer_stride;
+        a.v_rs = v_row_stride;
+        a.positions = positions;
+        a.cos_sin = cos_sin;
+        a.max_position = cos_sin ? max_position : 0;
+        for (int32_t i = 0; i < nrc::kMaxLayersPerLaunch; ++i) {
+            const int32_t l = first + (i < n ? i : 0);
+            a.layers.cache[i] = caches[l];
+            a.layers.slots[i] = slots[l];
+        }
+        a.layers_in_launch = (uint32_t)n;
+        a.rows = (uint32_t)rows;
+        a.H = (uint32_t)H;
+        a.log2H = log2H;
+        a.block_size = bs;
+        a.bs_shift = bs_shift;
+        a.n_slots = (uint32_t)(num_blocks * block_size);
+        a.eps = eps;
+        const int st = launch_status(nrc::launch_kv_store(a, (hipStream_t)stream), "context_kv_store");
+        if (st) return st;
+    }
+    return NRC_OK;
+}
+
+int32_t nrc_check_scalars(const float* in, uint16_t* bf16_out, float* rsqrt_out, int64_t n, void* stream) {
+    if (n < 0) return fail(NRC_EINVAL, "check_scalars: n < 0");
+    if (n > ((int64_t)1 << 32)) return fail(NRC_EINVAL, "check_scalars: n > 2^32");
+    if (n == 0) return NRC_OK;
+    if (!in || (!bf16_out && !rsqrt_out)) return fail(NRC_EINVAL, "check_scalars: NULL operand");
+    return launch_status(nrc::launch_scalars(in, bf16_out, rsqrt_out, n, (hipStream_t)stream), "check_scalars");
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Device helpers shared by the libnrc kernels (gfx950 / CDNA4, wave64).
+//
+// Arithmetic contract (matches the chain as the vLLM context page's kernels
+// state it, with correctly rounded operations in place of the approximate
+// reciprocal square root):
+//   - every FP32 op rounds to nearest even; FMA only where written
+//     (__builtin_fmaf); the library builds with -ffp-contract=off;
+//   - f32 subnormals are kept (no flush-to-zero);
+//   - 1/sqrt(v) is a correctly rounded sqrt followed by a correctly rounded
+//     divide;
+//   - f32 -> bf16 rounds to nearest even on the bit pattern; every NaN
+//     becomes 0x7FC0.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nrc {
+
+constexpr int kHidden = 8192;
+constexpr int kHeadDim = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// f32 -> bf16 bits, round to nearest even; NaN -> 0x7FC0.
+__device__ __forceinline__ uint32_t to_bf16(float x) {
+    uint32_t u = __float_as_uint(x);
+    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : r;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return to_bf16(lo) | (to_bf16(hi) << 16); }
+
+// 1/sqrt(v): llvm.sqrt.f32 and fdiv without fast-math flags lower to the
+// correctly rounded gfx9 sequences (checked exhaustively by the GPU tests).
+__device__ __forceinline__ float rsqrt_rn(float v) { return 1.0f / __builtin_sqrtf(v); }
+
+// Cross-lane exchange inside a wave64 (value of lane ^ MASK). MASK 1 and 2
+// use DPP quad permutes, MASK 4/8/16 a ds_swizzle xor pattern (within 32
+// lanes), MASK 32 a bpermute.
+template <int MASK>
+__device__ __forceinline__ float lane_xor(float v) {
+    int x = __float_as_int(v);
+    if constexpr (MASK == 1) {
+        x = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+    } else if constexpr (MASK == 2) {
+        x = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+    } else if constexpr (MASK == 4 || MASK == 8 || MASK == 16) {
+        x = __builtin_amdgcn_ds_swizzle(x, (MASK << 10) | 0x1F);  // bitmask mode: and 0x1F, xor MASK
+    } else {
+        static_assert(MASK == 32, "lane_xor: mask 1, 2, 4, 8, 16 or 32");
+        x = __builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 32u) << 2), x);
+    }
+    return __int_as_float(x);
+}
+
+// Fold by halves over the 64 lanes of a wave (strides 32, 16, 8, 4, 2, 1);
+// IEEE addition commutes, so both lanes of each pair hold the same sum and
+// every lane ends with the fold's value.
+__device__ __forceinline__ float wave_fold64(float v) {
+    v = v + lane_xor<32>(v);
+    v = v + lane_xor<16>(v);
+    v = v + lane_xor<8>(v);
+    v = v + lane_xor<4>(v);
+    v = v + lane_xor<2>(v);
+    v = v + lane_xor<1>(v);
+    return v;
+}
+
+struct alignas(16) U32x4 {
+    uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ U32x4 load16(const void* p) {
+    return *reinterpret_cast<const U32x4*>(p);
+}
+__device__ __forceinline__ void store16(void* p, U32x4 v) { *reinterpret_cast<U32x4*>(p) = v; }
+
+__device__ __forceinline__ U32x4 load16_nt(const void* p) {
+    const U32x4* q = reinterpret_cast<const U32x4*>(p);
+    U32x4 v;
+    v.x = __builtin_nontemporal_load(&q->x);
+    v.y = __builtin_nontemporal_load(&q->y);
+    v.z = __builtin_nontemporal_load(&q->z);
+    v.w = __builtin_nontemporal_load(&q->w);
+    return v;
+}
+
+__device__ __forceinline__ void store16_nt(void* p, U32x4 v) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
+}
+
+}  // namespace nrc

@@ -1,0 +1,63 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Arguments reach these functions already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nrc {
+
+constexpr int kMaxLayersPerLaunch = 8;
+
+struct StoreLayers {
+    uint16_t* cache[kMaxLayersPerLaunch];
+    const int64_t* slots[kMaxLayersPerLaunch];
+};
+
+struct KvStoreArgs {
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t k_ls, k_rs, v_ls, v_rs;
+    const int64_t* positions;
+    const uint16_t* cos_sin;  // nullptr: RoPE off
+    int64_t max_position;
+    StoreLayers layers;
+    uint32_t layers_in_launch;
+    uint32_t rows;
+    uint32_t H;
+    uint32_t log2H;
+    uint32_t block_size;
+    int32_t bs_shift;  // log2(block_size), or -1 when not a power of two
+    uint32_t n_slots;
+    float eps;
+};
+
+int launch_kv_store(const KvStoreArgs& a, hipStream_t stream);
+
+struct NormsArgs {
+    const uint16_t* x;
+    int64_t T;
+    const uint16_t* hidden_w;  // nullptr: weightless
+    const uint16_t* pre_w;     // nullptr: weightless
+    int32_t L;
+    float hidden_eps, pre_eps, hidden_center, pre_center;
+    uint16_t* out;
+    int32_t num_cus;
+};
+
+int launch_context_norms(const NormsArgs& a, hipStream_t stream);
+
+struct ProjectArgs {
+    const uint16_t* A;  // [L, M, K]
+    const uint16_t* B;  // [L, K, N]
+    uint16_t* C;        // [L, M, N]
+    int32_t L;
+    int64_t M, K, N;
+    int32_t num_cus;
+};
+
+int launch_kv_project(const ProjectArgs& a, hipStream_t stream);
+
+int launch_scalars(const float* in, uint16_t* bf, float* rs, int64_t n, hipStream_t stream);
+
+}  // namespace nrc

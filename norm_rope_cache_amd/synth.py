@@ -129,6 +129,24 @@ def random_bits_u16(seed, shape):
     return z.view(np.uint16)[:n].reshape(shape)
 
 
+def bf16_bits_range(seed, shape, emin=-6):
+    """Random bf16 bit patterns built directly (no rounding): random sign,
+    exponent uniform in [emin, emin + 7], random 7-bit mantissa. A fast
+    stand-in for large activation tensors."""
+    n = int(np.prod(shape))
+    out = random_bits_u16(seed, (n,))
+    base = np.uint16((emin + 127) << 7)
+
+    def one(i0):
+        v = out[i0:i0 + 4 * CHUNK]
+        e = (v >> np.uint16(7)) & np.uint16(7)
+        v &= np.uint16(0x807F)
+        v |= (e << np.uint16(7)) + base
+
+    _pool_map(one, list(range(0, n, 4 * CHUNK)))
+    return out.reshape(shape)
+
+
 def permutation(seed, n):
     """A seeded permutation of 0..n-1 (argsort of random keys, stable)."""
     return np.argsort(splitmix64(seed, n), kind="stable").astype(np.int64)
@@ -262,7 +280,7 @@ def slot_mapping(cfg):
     raise ValueError(cfg.name)
 
 
-def make_inputs(cfg, with_cache=True, kv_synth=False):
+def make_inputs(cfg, with_cache=True, kv_synth=False, with_x=True, with_weights=True):
     """All operands of one config (numpy, bf16 as uint16 bits).
 
     Returns a dict with x, hidden_w, pre_w, w_kv, cos_sin, positions, slots
@@ -273,7 +291,9 @@ def make_inputs(cfg, with_cache=True, kv_synth=False):
     NaN and Inf) to drive the store on its own."""
     L, T, H, N = cfg.L, cfg.T, cfg.H, cfg.N
     out = {"cfg": cfg, "hidden_eps": 1e-6, "pre_eps": 1e-6, "k_eps": 1e-6}
-    if cfg.edge:
+    if not with_x:
+        pass
+    elif cfg.edge:
         x = edge_mixture_bf16(cfg.stream(TID_MIX), cfg.stream(TID_X), (T, D))
         nz = max(1, int(round(0.01 * T)))
         zrows = permutation(cfg.stream(TID_ZROWS), T)[:nz]
@@ -281,10 +301,12 @@ def make_inputs(cfg, with_cache=True, kv_synth=False):
         out["zero_rows"] = np.sort(zrows)
     else:
         x = normal_bf16(cfg.stream(TID_X), (T, D), std=cfg.x_std)
-    out["x"] = x
-    out["hidden_w"] = normal_bf16(cfg.stream(TID_HW), (D,), mean=1.0, std=0.1) if cfg.hidden_weighted else None
-    out["pre_w"] = normal_bf16(cfg.stream(TID_PW), (L, D), mean=1.0, std=0.1) if cfg.pre_weighted else None
-    out["w_kv"] = normal_bf16(cfg.stream(TID_W), (L, D, N), std=0.02)
+    if with_x:
+        out["x"] = x
+    if with_weights:
+        out["hidden_w"] = normal_bf16(cfg.stream(TID_HW), (D,), mean=1.0, std=0.1) if cfg.hidden_weighted else None
+        out["pre_w"] = normal_bf16(cfg.stream(TID_PW), (L, D), mean=1.0, std=0.1) if cfg.pre_weighted else None
+        out["w_kv"] = normal_bf16(cfg.stream(TID_W), (L, D, N), std=0.02)
     out["cos_sin"] = rope_table(cfg.max_position) if cfg.rope else None
     out["positions"] = positions(cfg)
     s = slot_mapping(cfg)

@@ -1,0 +1,128 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/nrc.h declares, and rejects bad arguments on the host before any
+launch (so these calls never touch a device)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nrc.h")
+
+EINVAL, ENOTSUP = -22, -95
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int32_t|const char\*|void)\s+(nrc_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import norm_rope_cache_amd as m
+
+    if not os.path.exists(m.library_path()):
+        from norm_rope_cache_amd import build
+
+        build.build()
+    return m._load()
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for s in ("nrc_context_norms", "nrc_context_kv_project", "nrc_context_kv_store", "nrc_last_error"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for s in declared_symbols():
+        assert hasattr(lib, s), s
+
+
+def test_abi_version(lib):
+    assert lib.nrc_abi_version() == 1
+
+
+def _err(lib):
+    return lib.nrc_last_error().decode()
+
+
+FAKE = ctypes.c_void_p(0x10000)  # an aligned non-NULL address that is never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10002)
+
+
+def test_norms_argument_checks(lib):
+    f = lib.nrc_context_norms
+    assert f(FAKE, 4, 4096, None, None, 1, 1e-6, 1e-6, 0.0, 0.0, FAKE, None) == ENOTSUP
+    assert "8192" in _err(lib)
+    assert f(FAKE, -1, 8192, None, None, 1, 1e-6, 1e-6, 0.0, 0.0, FAKE, None) == EINVAL
+    assert f(FAKE, 4, 8192, None, None, 0, 1e-6, 1e-6, 0.0, 0.0, FAKE, None) == EINVAL
+    assert f(None, 4, 8192, None, None, 1, 1e-6, 1e-6, 0.0, 0.0, FAKE, None) == EINVAL
+    assert f(MISALIGNED, 4, 8192, None, None, 1, 1e-6, 1e-6, 0.0, 0.0, FAKE, None) == EINVAL
+    assert f(FAKE, 4, 8192, MISALIGNED, None, 1, 1e-6, 1e-6, 0.0, 0.0, FAKE, None) == EINVAL
+    # T == 0 is a no-op that touches nothing
+    assert f(None, 0, 8192, None, None, 3, 1e-6, 1e-6, 0.0, 0.0, None, None) == 0
+
+
+def test_project_argument_checks(lib):
+    f = lib.nrc_context_kv_project
+    assert f(FAKE, FAKE, FAKE, 0, 8, 8192, 1024, None) == EINVAL
+    assert f(FAKE, FAKE, FAKE, 1, -1, 8192, 1024, None) == EINVAL
+    assert f(FAKE, FAKE, FAKE, 1, 8, 8100, 1024, None) == ENOTSUP
+    assert f(FAKE, FAKE, FAKE, 1, 8, 8192, 1000, None) == ENOTSUP
+    assert f(FAKE, None, FAKE, 1, 8, 8192, 1024, None) == EINVAL
+    assert f(FAKE, FAKE, MISALIGNED, 1, 8, 8192, 1024, None) == EINVAL
+    assert f(None, None, None, 2, 0, 8192, 1024, None) == 0
+
+
+def _store(lib, **kw):
+    a = dict(k=FAKE, v=FAKE, kls=1024 * 16, krs=1024, vls=1024 * 16, vrs=1024, pos=FAKE, slots=None, rows=16,
+             T=16, cs=FAKE, maxp=4096, caches=None, nb=64, bs=16, H=8, L=2, eps=1e-6)
+    a.update(kw)
+    L = a["L"]
+    arr = ctypes.c_void_p * max(L, 1)
+    slots = a["slots"] if a["slots"] is not None else arr(*([0x20000] * max(L, 1)))
+    caches = a["caches"] if a["caches"] is not None else arr(*([0x30000] * max(L, 1)))
+    return lib.nrc_context_kv_store(a["k"], a["v"], a["kls"], a["krs"], a["vls"], a["vrs"], a["pos"], slots,
+                                    a["rows"], a["T"], a["cs"], a["maxp"], caches, a["nb"], a["bs"], a["H"], L,
+                                    a["eps"], None)
+
+
+def test_store_argument_checks(lib):
+    assert _store(lib, L=0) == EINVAL
+    assert _store(lib, H=0) == EINVAL
+    assert _store(lib, H=6) == ENOTSUP
+    assert "power of two" in _err(lib)
+    assert _store(lib, rows=17) == EINVAL
+    assert _store(lib, rows=-1) == EINVAL
+    assert _store(lib, nb=1 << 27, bs=16) == ENOTSUP  # 2^31 slots
+    assert _store(lib, nb=0) == EINVAL
+    assert _store(lib, k=None) == EINVAL
+    assert _store(lib, v=MISALIGNED) == EINVAL
+    assert _store(lib, krs=1020) == EINVAL  # not a multiple of 8 elements
+    assert _store(lib, pos=None) == EINVAL  # RoPE without positions
+    assert _store(lib, maxp=0) == EINVAL
+    arr = ctypes.c_void_p * 2
+    assert _store(lib, slots=arr(0x20000, 0)) == EINVAL  # NULL slots of layer 1
+    assert _store(lib, caches=arr(0x30000, 0x30008)) == EINVAL  # misaligned cache of layer 1
+    # rows == 0 (and T == 0) are no-ops that touch nothing
+    assert _store(lib, rows=0, k=None, v=None, slots=None) == 0
+    assert _store(lib, rows=0, T=0) == 0
+
+
+def test_check_scalars_argument_checks(lib):
+    assert lib.nrc_check_scalars(FAKE, None, None, 4, None) == EINVAL
+    assert lib.nrc_check_scalars(FAKE, FAKE, None, -1, None) == EINVAL
+    assert lib.nrc_check_scalars(None, None, None, 0, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    """No fallback path: with libnrc.so missing, every call raises."""
+    import norm_rope_cache_amd as m
+
+    monkeypatch.setattr(m, "_lib", None)
+    monkeypatch.setattr(m, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        m.abi_version()

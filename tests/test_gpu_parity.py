@@ -1,0 +1,423 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: bit-exact for the norms, the K-norm/RoPE/insert and the scalar
+primitives; the projection within 1e-2 relative of the oracle's FP32 sums
+(per layer in Frobenius norm and per element against |C*| + the row's RMS).
+Inputs come from the seeded generator (norm_rope_cache_amd.synth) and are
+handed to both sides; nothing the HIP path computes feeds the oracle.
+"""
+
+import numpy as np
+import pytest
+
+from helpers import assert_bits_equal, f32, projection_tolerance_ok, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def nrc():
+    import norm_rope_cache_amd as m
+
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    m._load()
+    return m
+
+
+@pytest.fixture(scope="module")
+def oracle():
+    import oracle as o
+
+    o.lib()
+    return o
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------ scalar primitives
+
+def test_scalars_exhaustive(nrc, oracle):
+    """The device bf16 rounding and 1/sqrt on all 2^32 f32 patterns equal the
+    oracle's (NaN results compared as NaN for 1/sqrt)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    step = 1 << 27
+    pool = ThreadPoolExecutor(8)
+    for start in range(0, 1 << 32, step):
+        _say(f"scalars chunk {start:#x}")
+        bits = np.arange(step, dtype=np.uint32) + np.uint32(start)
+        x = bits.view(np.float32)
+        xd = torch.from_numpy(x).cuda()
+        bf, rs = nrc.check_scalars(xd)
+        gb = bf.cpu().numpy().view(np.uint16)
+        gr = rs.cpu().numpy()
+        parts = np.array_split(np.arange(step), 8)
+        ob = np.empty(step, dtype=np.uint16)
+        orr = np.empty(step, dtype=np.float32)
+
+        def one(ix):
+            ob[ix[0]:ix[-1] + 1] = oracle.bf16(x[ix[0]:ix[-1] + 1])
+            orr[ix[0]:ix[-1] + 1] = oracle.rs(x[ix[0]:ix[-1] + 1])
+
+        list(pool.map(one, parts))
+        assert_bits_equal(gb, ob, f"bf16 chunk {start:#x}")
+        same = (gr.view(np.uint32) == orr.view(np.uint32)) | (np.isnan(gr) & np.isnan(orr))
+        if not same.all():
+            i = int(np.nonzero(~same)[0][0])
+            raise AssertionError(f"rsqrt at {bits[i]:#x}: {gr[i]!r} vs {orr[i]!r}")
+
+
+# --------------------------------------------------------------------- norms
+
+NORM_CASES = ["tiny", "prefill", "weightless", "long", "edge"]
+
+
+def _norms_inputs(name):
+    from norm_rope_cache_amd import synth
+
+    cfg = synth.CONFIGS[name]
+    d = synth.make_inputs(cfg, with_cache=False)
+    return cfg, d
+
+
+@pytest.mark.parametrize("name", NORM_CASES)
+def test_norms_parity_configs(nrc, oracle, name):
+    """Full-size norms, bit-exact. The edge config is compared on a sample of
+    rows (every all-zero row, every row with a finite hidden sum, and a
+    seeded sample) plus a whole-output property: rows whose squares overflow
+    are signed zeros."""
+    cfg, d = _norms_inputs(name)
+    _say(f"norms {name}: L={cfg.L} T={cfg.T}")
+    x = to_dev(d["x"])
+    hw = None if d["hidden_w"] is None else to_dev(d["hidden_w"])
+    pw = None if d["pre_w"] is None else to_dev(d["pre_w"])
+    out = nrc.context_norms(x, hw, pw, cfg.L, d["hidden_eps"], d["pre_eps"])
+    torch.cuda.synchronize()
+    if name != "edge":
+        want = oracle.context_norms(d["x"], d["hidden_w"], d["pre_w"], cfg.L, d["hidden_eps"], d["pre_eps"])
+        assert_bits_equal(to_host(out), want, f"norms {name}")
+        return
+    xf = f32(d["x"])
+    finite_rows = np.nonzero(np.isfinite((xf.astype(np.float64) ** 2).sum(axis=1)) &
+                             (np.abs(xf).max(axis=1) < 1e18))[0]
+    rng = np.random.default_rng(99)
+    rows = np.unique(np.concatenate([d["zero_rows"], finite_rows, rng.choice(cfg.T, 512, replace=False)]))
+    want = oracle.context_norms(d["x"][rows], d["hidden_w"], d["pre_w"], cfg.L, d["hidden_eps"], d["pre_eps"])
+    got = to_host(out[:, torch.from_numpy(rows).cuda()])
+    assert_bits_equal(got, want, "norms edge (sampled rows)")
+
+
+@pytest.mark.parametrize("T", [1, 3, 37, 1000])
+@pytest.mark.parametrize("L,hw,pw", [(1, True, True), (2, False, True), (3, True, False), (5, False, False),
+                                     (8, True, True), (9, True, True), (12, False, True)])
+def test_norms_shapes(nrc, oracle, T, L, hw, pw):
+    from norm_rope_cache_amd import synth
+
+    seed = 1000 + 17 * T + L
+    x = synth.normal_bf16(seed, (T, 8192), std=1.3)
+    w_h = synth.normal_bf16(seed + 1, (8192,), 1.0, 0.1) if hw else None
+    w_p = synth.normal_bf16(seed + 2, (L, 8192), 1.0, 0.1) if pw else None
+    _say(f"norms T={T} L={L} hw={hw} pw={pw}")
+    out = nrc.context_norms(to_dev(x), None if w_h is None else to_dev(w_h), None if w_p is None else to_dev(w_p), L,
+                            1e-6, 1e-5)
+    want = oracle.context_norms(x, w_h, w_p, L, 1e-6, 1e-5)
+    assert_bits_equal(to_host(out), want, f"norms T={T} L={L}")
+
+
+def test_norms_special_values(nrc, oracle):
+    """-0.0, subnormals, near-max values, Inf, NaN, zero rows, -0.0 weights,
+    non-zero gain centers and eps = 0."""
+    from norm_rope_cache_amd import synth
+
+    T, L = 64, 3
+    x = synth.edge_mixture_bf16(77, 78, (T, 8192), nan_inf=True)
+    x[5] = 0
+    x[6] = 0x8000
+    x[7] = synth.edge_mixture_bf16(79, 80, (8192,))  # mixture without NaN/Inf
+    x[8, :] = 0x0001  # all smallest subnormals
+    x[9, :] = 0x7F7F  # all near max
+    x[10] = synth.normal_bf16(81, (8192,))
+    x[11] = synth.normal_bf16(82, (8192,), std=1e-20)
+    hw = synth.normal_bf16(83, (8192,), 1.0, 0.5)
+    hw[::97] = 0x8000
+    pw = synth.normal_bf16(84, (L, 8192), 1.0, 0.5)
+    pw[:, ::89] = 0x8000
+    pw[1, 5] = 0x0003
+    for he, pe, hc, pc in [(1e-6, 1e-6, 0.0, 0.0), (0.0, 0.0, 0.0, 0.0), (1e-6, 1e-6, 1.0, -0.5),
+                           (1e-6, 1e-6, -0.0, -0.0)]:
+        _say(f"norms specials eps={he},{pe} centers={hc},{pc}")
+        out = nrc.context_norms(to_dev(x), to_dev(hw), to_dev(pw), L, he, pe, hc, pc)
+        want = oracle.context_norms(x, hw, pw, L, he, pe, hc, pc)
+        assert_bits_equal(to_host(out), want, f"norms specials {he},{pe},{hc},{pc}")
+
+
+# ---------------------------------------------------------------- projection
+
+def _project_check(nrc, oracle, A, B, rows=None, what=""):
+    Ad, Bd = to_dev(A), to_dev(B)
+    C = to_host(nrc.context_kv_project(Ad, Bd))
+    if rows is not None:
+        A_s = np.ascontiguousarray(A[:, rows])
+        Cstar = oracle.kv_project(A_s, B)
+        C = C[:, rows]
+    else:
+        Cstar = oracle.kv_project(A, B)
+    ok, msg = projection_tolerance_ok(C, Cstar)
+    assert ok, f"{what}: {msg}"
+    return C
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill", "weightless", "long", "edge"])
+def test_project_parity_configs(nrc, oracle, name):
+    """Full-size projection of every config (the bench's launch shape for
+    the long config), checked on sampled rows against the oracle's FP32
+    sums."""
+    from norm_rope_cache_amd import synth
+
+    cfg = synth.CONFIGS[name]
+    _say(f"project {name}: L={cfg.L} T={cfg.T} N={cfg.N}")
+    A = synth.bf16_bits_range(cfg.stream(31), (cfg.L, cfg.T, 8192), emin=-4)
+    B = synth.normal_bf16(cfg.stream(synth.TID_W), (cfg.L, 8192, cfg.N), std=0.02)
+    rng = np.random.default_rng(cfg.index)
+    n = min(cfg.T, 24 if cfg.N > 1024 else 64)
+    rows = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, n, replace=False)]))
+    _project_check(nrc, oracle, A, B, rows, f"project {name}")
+
+
+@pytest.mark.parametrize("T,N", [(1, 128), (5, 256), (37, 1024), (130, 128), (300, 2048), (513, 384), (1000, 1024)])
+def test_project_shapes(nrc, oracle, T, N):
+    from norm_rope_cache_amd import synth
+
+    L = 2
+    A = synth.normal_bf16(2000 + T, (L, T, 8192))
+    B = synth.normal_bf16(3000 + N, (L, 8192, N), std=0.02)
+    rows = None if T <= 64 else np.unique(np.concatenate([[0, T - 1], np.arange(1, T, max(1, T // 40))]))
+    _say(f"project T={T} N={N}")
+    _project_check(nrc, oracle, A, B, rows, f"project T={T} N={N}")
+
+
+def test_project_one_hot_and_zero_rows(nrc, oracle):
+    """A one-hot row selects a row of B: the result is that row's bf16 value
+    exactly; an all-zero row gives +0."""
+    from norm_rope_cache_amd import synth
+
+    L, T, N = 2, 300, 1024
+    B = synth.normal_bf16(4001, (L, 8192, N), std=0.02)
+    A = np.zeros((L, T, 8192), dtype=np.uint16)
+    cols = (np.arange(T) * 97) % 8192
+    for l in range(L):
+        A[l, np.arange(T - 10), cols[:T - 10]] = 0x3F80
+    C = to_host(nrc.context_kv_project(to_dev(A), to_dev(B)))
+    for l in range(L):
+        assert_bits_equal(C[l, :T - 10], B[l, cols[:T - 10]], f"one-hot rows layer {l}")
+        assert np.all(C[l, T - 10:] == 0)
+
+
+# -------------------------------------------------------------------- store
+
+def _store_case(name, T=None, kv_rows=4096):
+    from norm_rope_cache_amd import synth
+
+    cfg = synth.CONFIGS[name]
+    if T is not None:
+        cfg = synth.scaled(cfg, T)
+    d = synth.make_inputs(cfg, with_cache=True, kv_synth=cfg.T <= kv_rows, with_x=False, with_weights=False)
+    if "kv" not in d:
+        # a block of synthetic projection rows repeated over T (bounded generation)
+        if cfg.edge:
+            blk = synth.edge_mixture_bf16(cfg.stream(synth.TID_KVMIX), cfg.stream(synth.TID_KV),
+                                          (cfg.L, kv_rows, cfg.N), nan_inf=True)
+        else:
+            blk = synth.normal_bf16(cfg.stream(synth.TID_KV), (cfg.L, kv_rows, cfg.N), std=1.8)
+        reps = (cfg.T + kv_rows - 1) // kv_rows
+        d["kv"] = np.ascontiguousarray(np.tile(blk, (1, reps, 1))[:, :cfg.T])
+    return cfg, d
+
+
+def _run_store(nrc, oracle, cfg, d, rows=None, eps=1e-6):
+    caches_d = to_dev(d["caches"])
+    kv_d = to_dev(d["kv"])
+    slots = d["slots"] if rows is None else np.ascontiguousarray(d["slots"][:, :rows])
+    slots_d = to_dev(slots)
+    cs_d = None if d["cos_sin"] is None else to_dev(d["cos_sin"])
+    pos_d = to_dev(d["positions"])
+    nrc.context_kv_store(kv_d, pos_d, slots_d, cs_d, caches_d, cfg.H, eps)
+    torch.cuda.synchronize()
+    got = to_host(caches_d)
+    want = d["caches"].copy()
+    oracle.context_kv_store(d["kv"], cfg.H, d["positions"], slots, d["cos_sin"], want, cfg.block_size, eps)
+    return got, want
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill", "weightless", "long", "edge"])
+def test_store_parity_configs(nrc, oracle, name):
+    """Full-size K-norm + RoPE + insert, bit-exact over every cache cell
+    (untouched cells keep their prior random bits)."""
+    cfg, d = _store_case(name)
+    _say(f"store {name}: L={cfg.L} T={cfg.T} H={cfg.H} bs={cfg.block_size} nb={cfg.num_blocks}")
+    got, want = _run_store(nrc, oracle, cfg, d)
+    assert_bits_equal(got, want, f"store {name}")
+
+
+def test_store_from_oracle_projection(nrc, oracle):
+    """The store on a realistic projection output: the oracle's chain up to
+    the projection (norms, FP32 sums, bf16) feeds both sides."""
+    from norm_rope_cache_amd import synth
+
+    cfg = synth.scaled(synth.PREFILL, 64)
+    d = synth.make_inputs(cfg, with_cache=True)
+    normed = oracle.context_norms(d["x"], d["hidden_w"], d["pre_w"], cfg.L)
+    d["kv"] = oracle.bf16(oracle.kv_project(normed, d["w_kv"]))
+    got, want = _run_store(nrc, oracle, cfg, d)
+    assert_bits_equal(got, want, "store on the oracle's projection")
+
+
+def test_store_rows_subset_and_rope_off(nrc, oracle):
+    """Only the first `rows` rows are inserted; RoPE off stores the K-norm."""
+    cfg, d = _store_case("tiny")
+    for rows in (0, 1, 7, 16):
+        _say(f"store tiny rows={rows}")
+        got, want = _run_store(nrc, oracle, cfg, d, rows=rows)
+        assert_bits_equal(got, want, f"store rows={rows}")
+    d["cos_sin"] = None
+    got, want = _run_store(nrc, oracle, cfg, d)
+    assert_bits_equal(got, want, "store rope off")
+
+
+@pytest.mark.parametrize("L,H,bs,nb", [(10, 2, 24, 9), (3, 4, 7, 50), (9, 1, 1, 300), (2, 32, 5, 60)])
+def test_store_shapes(nrc, oracle, L, H, bs, nb):
+    """More than 8 layers (two launches), block sizes that are not powers of
+    two, 1..32 heads, per-layer slot mappings."""
+    from norm_rope_cache_amd import synth
+
+    T = 200
+    N = 2 * H * 64
+    rng = np.random.default_rng(L * 1000 + H)
+    kv = synth.normal_bf16(5000 + L + H, (L, T, N), std=1.8)
+    slots = np.stack([rng.permutation(nb * bs)[:T] for _ in range(L)]).astype(np.int64)
+    slots[rng.random((L, T)) < 0.2] = -1
+    positions = rng.integers(0, 512, T).astype(np.int64)
+    tab = synth.rope_table(512)
+    caches = synth.random_bits_u16(6000 + L, (L, nb, H, bs, 128))
+    for eps in (1e-6, 0.0, 0.25):
+        _say(f"store shapes L={L} H={H} bs={bs} nb={nb} eps={eps}")
+        cd = to_dev(caches)
+        nrc.context_kv_store(to_dev(kv), to_dev(positions), [to_dev(s) for s in slots], to_dev(tab),
+                             [cd[i] for i in range(L)], H, eps)
+        want = caches.copy()
+        oracle.context_kv_store(kv, H, positions, slots, tab, want, bs, eps)
+        assert_bits_equal(to_host(cd), want, f"store L={L} H={H} bs={bs} eps={eps}")
+
+
+def test_store_strided_views(nrc, oracle):
+    """k and v as views with padded row and layer strides."""
+    from norm_rope_cache_amd import synth
+
+    L, T, H, bs, nb = 3, 50, 2, 16, 8
+    N = 2 * H * 64
+    kv = synth.normal_bf16(7001, (L, T, N), std=1.8)
+    big = np.zeros((L + 1, T + 3, N + 64), dtype=np.uint16)
+    big[:L, :T, :N] = kv
+    bd = to_dev(big)
+    k = bd[:L, :T, :H * 64].unflatten(2, (H, 64))
+    v = bd[:L, :T, H * 64:N].unflatten(2, (H, 64))
+    rng = np.random.default_rng(3)
+    slots = np.stack([rng.permutation(nb * bs)[:T] for _ in range(L)]).astype(np.int64)
+    positions = np.arange(T, dtype=np.int64)
+    tab = synth.rope_table(64)
+    caches = synth.random_bits_u16(7002, (L, nb, H, bs, 128))
+    cd = to_dev(caches)
+    nrc.context_kv_store(None, to_dev(positions), to_dev(slots), to_dev(tab), cd, H, 1e-6, k=k, v=v)
+    want = caches.copy()
+    oracle.context_kv_store(kv, H, positions, slots, tab, want, bs, 1e-6)
+    assert_bits_equal(to_host(cd), want, "store strided views")
+
+
+def test_store_skips_out_of_range_rows(nrc, oracle):
+    """Rows whose slot or position breaks the range preconditions are skipped
+    by the kernel's own bounds checks (nothing is written out of bounds)."""
+    from norm_rope_cache_amd import synth
+
+    L, T, H, bs, nb = 2, 40, 2, 16, 4
+    kv = synth.normal_bf16(8001, (L, T, 256), std=1.8)
+    rng = np.random.default_rng(5)
+    slots = np.stack([rng.permutation(nb * bs)[:T] for _ in range(L)]).astype(np.int64)
+    positions = rng.integers(0, 100, T).astype(np.int64)
+    tab = synth.rope_table(100)
+    bad_slot = slots.copy()
+    bad_slot[0, 3] = nb * bs + 5
+    bad_slot[1, 4] = 1 << 40
+    bad_pos = positions.copy()
+    bad_pos[7] = 100
+    bad_pos[8] = -3
+    caches = synth.random_bits_u16(8002, (L, nb, H, bs, 128))
+    cd = to_dev(caches)
+    nrc.context_kv_store(to_dev(kv), to_dev(bad_pos), to_dev(bad_slot), to_dev(tab), cd, H, 1e-6)
+    # expected: the oracle on the valid rows only (skipped rows as slot -1)
+    ok_slots = bad_slot.copy()
+    ok_slots[0, 3] = -1
+    ok_slots[1, 4] = -1
+    ok_slots[:, 7] = -1
+    ok_slots[:, 8] = -1
+    ok_pos = positions.copy()
+    want = caches.copy()
+    oracle.context_kv_store(kv, H, ok_pos, ok_slots, tab, want, bs, 1e-6)
+    assert_bits_equal(to_host(cd), want, "store with out-of-range rows")
+
+
+# --------------------------------------------------------------------- chain
+
+@pytest.mark.parametrize("name,T", [("tiny", 16), ("prefill", 48), ("weightless", 40)])
+def test_chain_parity(nrc, oracle, name, T):
+    """The chain through all three calls against the oracle's chain: norms
+    bit-exact, projection within tolerance, cache cells written exactly where
+    the oracle writes them, with K and V within the projection's tolerance
+    and every other cell untouched."""
+    from norm_rope_cache_amd import synth
+
+    cfg = synth.scaled(synth.CONFIGS[name], T)
+    d = synth.make_inputs(cfg, with_cache=True)
+    _say(f"chain {name} T={T}")
+    caches_d = to_dev(d["caches"])
+    normed, kv = nrc.context_kv_chain(
+        to_dev(d["x"]), None if d["hidden_w"] is None else to_dev(d["hidden_w"]),
+        None if d["pre_w"] is None else to_dev(d["pre_w"]), to_dev(d["w_kv"]), to_dev(d["positions"]),
+        to_dev(d["slots"]), None if d["cos_sin"] is None else to_dev(d["cos_sin"]), caches_d, cfg.H)
+    torch.cuda.synchronize()
+    want_caches = d["caches"].copy()
+    o_normed, o_kv = oracle.chain(d["x"], d["hidden_w"], d["pre_w"], cfg.L, d["w_kv"], cfg.H, d["positions"],
+                                  d["slots"], d["cos_sin"], want_caches, cfg.block_size)
+    assert_bits_equal(to_host(normed), o_normed, f"chain norms {name}")
+    ok, msg = projection_tolerance_ok(to_host(kv), oracle.kv_project(o_normed, d["w_kv"]))
+    assert ok, msg
+    got_caches = to_host(caches_d)
+    written = np.any(want_caches != d["caches"], axis=-1) | np.any(got_caches != d["caches"], axis=-1)
+    assert_bits_equal(got_caches[~written], d["caches"][~written], "untouched cells")
+    # every written cell: K within tolerance of the oracle's K, V likewise
+    gw = f32(got_caches[written]).astype(np.float64)
+    ww = f32(want_caches[written]).astype(np.float64)
+    err = np.abs(gw - ww)
+    assert np.all(err <= 2e-2 * (np.abs(ww) + np.sqrt(np.mean(ww ** 2, axis=-1, keepdims=True)))), \
+        f"chain cache values: max error {err.max()}"
+
+
+def test_deterministic(nrc):
+    """Two runs of the chain give identical bits."""
+    from norm_rope_cache_amd import synth
+
+    cfg = synth.scaled(synth.PREFILL, 300)
+    d = synth.make_inputs(cfg, with_cache=True)
+    outs = []
+    for _ in range(2):
+        cd = to_dev(d["caches"])
+        normed, kv = nrc.context_kv_chain(to_dev(d["x"]), to_dev(d["hidden_w"]), to_dev(d["pre_w"]),
+                                          to_dev(d["w_kv"]), to_dev(d["positions"]), to_dev(d["slots"]),
+                                          to_dev(d["cos_sin"]), cd, cfg.H)
+        outs.append((to_host(normed), to_host(kv), to_host(cd)))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
