@@ -95,6 +95,8 @@ def main():
     ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy 1 GiB device-to-device once, a known-size reference for HBM byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -145,6 +147,15 @@ def main():
         nrc.context_kv_store(kv, positions, slots, cos_sin, caches, cfg.H, d["k_eps"])
         if ev:
             ev[3].record()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev).random_(-32768, 32767)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 1 GiB read + 1 GiB written")
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
