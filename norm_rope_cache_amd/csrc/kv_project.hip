@@ -19,6 +19,8 @@
 //   - Tiles are ordered layer, M tile, N tile (N fastest); consecutive tile
 //     ids are assigned to the same XCD (workgroup ids are dealt round-robin
 //     over the 8 XCDs), so the N tiles sharing an A panel meet in one L2.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -27,47 +29,68 @@ namespace nrc {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kThreads = 256;
-constexpr int kBK = 64;       // K per LDS stage
-constexpr int kRowChunks = 8; // 16-byte chunks per LDS row (64 bf16)
+constexpr int kBK = 32;     // K per LDS stage
+constexpr int kStages = 4;  // LDS ring depth
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-
-// LDS address (in 16-byte units) of chunk c of row r.
-__device__ __forceinline__ int lds_chunk(int r, int c) { return r * kRowChunks + (c ^ swz(r)); }
-
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
-
-template <int BM, int BN>
-struct Tile {
-    static constexpr int MI = BM / 64;          // 32-row MFMA blocks per wave (wave tile BM/2 rows)
-    static constexpr int NI = BN / 64;          // 32-col MFMA blocks per wave
-    static constexpr int A_PER_THREAD = BM / 32;  // 16-byte A chunks per thread per stage
-    static constexpr int NPT = BN / 32;         // B columns per thread (4 or 8)
-    static constexpr int A_CHUNKS = BM * kRowChunks;
-    static constexpr int B_CHUNKS = BN * kRowChunks;
-    static constexpr int STAGE_CHUNKS = A_CHUNKS + B_CHUNKS;
+template <int BM, int BN, int WM, int WN>
+struct Cfg {
+    static constexpr int WAVES = WM * WN;              // waves per workgroup, WM along M x WN along N
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int WTM = BM / WM, WTN = BN / WN; // wave tile
+    static constexpr int MI = WTM / 32;                // 32-row MFMA blocks per wave
+    static constexpr int NI = WTN / 32;                // 32-column MFMA blocks per wave
+    static constexpr int A_BYTES = BM * kBK * 2;       // one stage of A: BM rows x 64 bytes
+    static constexpr int B_BYTES = kBK * BN * 2;       // one stage of B: 32 k rows x 2 BN bytes
+    static constexpr int B_ROW = BN * 2;
+    static constexpr int A_LOADS = A_BYTES / 1024 / WAVES;  // 1 KiB DMA blocks per wave per stage
+    static constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
+    static constexpr int LOADS = A_LOADS + B_LOADS;
+    static constexpr int A_REGION = kStages * A_BYTES;
+    static constexpr int LDS_BYTES = kStages * (A_BYTES + B_BYTES);
+    static_assert(A_LOADS >= 1 && B_LOADS >= 1 && A_LOADS * WAVES * 1024 == A_BYTES &&
+                      B_LOADS * WAVES * 1024 == B_BYTES,
+                  "tile must split into whole 1 KiB DMA blocks per wave");
 };
 
-template <int BM, int BN>
-__global__ __launch_bounds__(kThreads) void kv_project_kernel(const uint16_t* __restrict__ A,
+// s_waitcnt immediates (gfx9 encoding: vmcnt in [3:0] and [15:14], expcnt
+// in [6:4], lgkmcnt in [11:8]); the counters not named are left at their
+// maximum so they do not wait.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 *
+// lane (global_load_lds_dwordx4, gfx950). Issued as inline assembly so the
+// kernel alone accounts for these writes with explicit vmcnt waits and
+// barriers (the pipeline below), instead of a conservative wait for every
+// outstanding load before each LDS read.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t* __restrict__ A,
                                                               const uint16_t* __restrict__ B,
                                                               uint16_t* __restrict__ C, int64_t M, int64_t K,
                                                               int64_t N, int32_t tiles_m, int32_t tiles_n,
                                                               int32_t total_tiles) {
-    using TL = Tile<BM, BN>;
-    extern __shared__ U32x4 lds[];  // 2 stages of [A rows | B rows]
+    using CF = Cfg<BM, BN, WM, WN>;
+    extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
+    lds_char* lds = (lds_char*)lds_raw;
 
     // XCD-aware tile id: workgroup b runs on XCD b % 8; give each XCD a
-    // contiguous range of tiles.
+    // contiguous range of tiles (N fastest), so the N tiles that share an
+    // A panel run side by side under one L2.
     int tile = blockIdx.x;
-    if ((total_tiles & 7) == 0) {
-        const int per_xcd = total_tiles >> 3;
-        tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    }
+    if ((total_tiles & 7) == 0) tile = (blockIdx.x & 7) * (total_tiles >> 3) + (blockIdx.x >> 3);
     const int tn = tile % tiles_n;
     const int tm = (tile / tiles_n) % tiles_m;
     const int layer = tile / (tiles_n * tiles_m);
@@ -79,137 +102,158 @@ __global__ __launch_bounds__(kThreads) void kv_project_kernel(const uint16_t* __
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
 
-    // ---- global -> register staging assignments
-    // A: chunk column a_c = tid % 8, rows tid / 8 + 32 i (rows past M clamp to M-1).
-    const int a_c = tid & 7;
-    const uint16_t* a_src[TL::A_PER_THREAD];
+    // ---- DMA assignments (global -> LDS, 16 bytes per lane, 1 KiB per wave
+    // instruction written to consecutive LDS bytes). The global source of
+    // each lane is chosen so that LDS holds the swizzled layouts below.
+    //   A stage: row r (BM rows, 64 bytes = 4 chunks of 8 k), chunk c stored
+    //            at chunk c ^ ((r >> 1) & 3).
+    //   B stage: k row r (32 rows, 2 BN bytes), 16-byte chunk c stored at
+    //            chunk c ^ (2 (r & 3)).
+    const uint16_t* a_src[CF::A_LOADS];
 #pragma unroll
-    for (int i = 0; i < TL::A_PER_THREAD; ++i) {
-        int64_t r = m0 + (tid >> 3) + 32 * i;
-        r = r < M ? r : M - 1;
-        a_src[i] = Al + r * K + 8 * a_c;
+    for (int t = 0; t < CF::A_LOADS; ++t) {
+        const int off = (wave * CF::A_LOADS + t) * 1024 + lane * 16;
+        const int r = off >> 6, pc = (off >> 4) & 3;
+        const int c = pc ^ ((r >> 1) & 3);
+        int64_t row = m0 + r;
+        row = row < M ? row : M - 1;
+        a_src[t] = Al + row * K + 8 * c;
     }
-    // B: k rows 8 kb .. 8 kb + 7 of the stage, columns n0 + NPT nq .. + NPT.
-    const int nq = tid & 31, kb = tid >> 5;
-    const uint16_t* b_src = Bl + (int64_t)(8 * kb) * N + n0 + TL::NPT * nq;
-
-    U32x4 a_reg[TL::A_PER_THREAD];
-    U32x4 b_reg[8];  // NPT = 8: full 16 bytes; NPT = 4: x, y used
-
-    auto load_stage = [&](int64_t k0) {
+    const uint16_t* b_src[CF::B_LOADS];
 #pragma unroll
-        for (int i = 0; i < TL::A_PER_THREAD; ++i) a_reg[i] = load16(a_src[i] + k0);
+    for (int t = 0; t < CF::B_LOADS; ++t) {
+        const int off = (wave * CF::B_LOADS + t) * 1024 + lane * 16;
+        const int r = off / CF::B_ROW, pc = (off % CF::B_ROW) >> 4;
+        const int c = pc ^ (2 * (r & 3));
+        b_src[t] = Bl + (int64_t)r * N + n0 + 8 * c;
+    }
+    auto issue = [&](int s, int buf) {  // k stage s -> LDS buffer buf
+        const int64_t ka = (int64_t)s * kBK;
+        const int64_t kb = (int64_t)s * kBK * N;
+        const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const uint16_t* p = b_src + (k0 + r) * N;
-            if constexpr (TL::NPT == 8) {
-                b_reg[r] = load16(p);
-            } else {
-                const uint2 v = *reinterpret_cast<const uint2*>(p);
-                b_reg[r] = U32x4{v.x, v.y, 0u, 0u};
-            }
-        }
+        for (int t = 0; t < CF::A_LOADS; ++t)
+            dma16(a_src[t] + ka,
+                  __builtin_amdgcn_readfirstlane(base + buf * CF::A_BYTES + (wave * CF::A_LOADS + t) * 1024));
+#pragma unroll
+        for (int t = 0; t < CF::B_LOADS; ++t)
+            dma16(b_src[t] + kb, __builtin_amdgcn_readfirstlane(base + CF::A_REGION + buf * CF::B_BYTES +
+                                                                (wave * CF::B_LOADS + t) * 1024));
     };
 
-    auto store_stage = [&](int stage) {
-        U32x4* sa = lds + stage * TL::STAGE_CHUNKS;
-        U32x4* sb = sa + TL::A_CHUNKS;
+    // ---- MFMA operand reads.
+    // A (ds_read_b128): lane reads row wm BM/2 + 32 i + (lane & 31), k chunk
+    // 2 kk + (lane >> 5) of the 32-wide stage.
+    const int khalf = lane >> 5;
+    int a_off[2];
 #pragma unroll
-        for (int i = 0; i < TL::A_PER_THREAD; ++i) sa[lds_chunk((tid >> 3) + 32 * i, a_c)] = a_reg[i];
-        // Transpose the 8 x NPT block: column j collects k rows 0..7.
-        const uint32_t* w[8];
+    for (int kk = 0; kk < 2; ++kk) {
+        const int r = wm * CF::WTM + (lane & 31);
+        a_off[kk] = r * 64 + 16 * ((2 * kk + khalf) ^ ((r >> 1) & 3));
+    }
+    // B (ds_read_b64_tr_b16): within each 16-lane group g, lane c = 4 jj + q
+    // points at 4 bf16 of k row kbase + jj, columns 4 q .. 4 q + 3 of the
+    // group's 16 columns; the transposing read hands lane i of the group the
+    // 4 k values kbase .. kbase + 3 of column i. Groups 0/1 cover columns
+    // 0-15/16-31 of the block at k 0..7 of the sub-step, groups 2/3 k 8..15.
+    int b_off[CF::NI];
+    {
+        const int g = lane >> 4, c = lane & 15, jj = c >> 2, q = c & 3;
+        const int krow = 8 * (g >> 1) + jj;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) w[r] = &b_reg[r].x;
-#pragma unroll
-        for (int j = 0; j < TL::NPT; ++j) {
-            U32x4 col;
-            if ((j & 1) == 0) {
-                col.x = lo_pair(w[0][j >> 1], w[1][j >> 1]);
-                col.y = lo_pair(w[2][j >> 1], w[3][j >> 1]);
-                col.z = lo_pair(w[4][j >> 1], w[5][j >> 1]);
-                col.w = lo_pair(w[6][j >> 1], w[7][j >> 1]);
-            } else {
-                col.x = hi_pair(w[0][j >> 1], w[1][j >> 1]);
-                col.y = hi_pair(w[2][j >> 1], w[3][j >> 1]);
-                col.z = hi_pair(w[4][j >> 1], w[5][j >> 1]);
-                col.w = hi_pair(w[6][j >> 1], w[7][j >> 1]);
-            }
-            sb[lds_chunk(TL::NPT * nq + j, kb)] = col;
+        for (int j = 0; j < CF::NI; ++j) {
+            const int n = wn * CF::WTN + 32 * j + 16 * (g & 1) + 4 * q;
+            const int pc = (n >> 3) ^ (2 * jj);
+            b_off[j] = CF::A_REGION + krow * CF::B_ROW + pc * 16 + ((n >> 2) & 1) * 8;
         }
-    };
+    }
 
-    f32x16 acc[TL::MI][TL::NI];
+    f32x16 acc[CF::MI][CF::NI];
 #pragma unroll
-    for (int i = 0; i < TL::MI; ++i)
+    for (int i = 0; i < CF::MI; ++i)
 #pragma unroll
-        for (int j = 0; j < TL::NI; ++j)
+        for (int j = 0; j < CF::NI; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    const int ksteps = (int)(K / kBK);
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-
-    // MFMA operand rows of this lane.
-    const int a_row0 = wm * (BM / 2) + (lane & 31);
-    const int b_row0 = wn * (BN / 2) + (lane & 31);
-    const int khalf = lane >> 5;  // lanes 32..63 hold k 8..15 of each 16-wide step
-
-    for (int ks = 0; ks < ksteps; ++ks) {
-        const int cur = ks & 1;
-        if (ks + 1 < ksteps) load_stage((int64_t)(ks + 1) * kBK);
-        const U32x4* sa = lds + cur * TL::STAGE_CHUNKS;
-        const U32x4* sb = sa + TL::A_CHUNKS;
+    bf16x8 af[2][CF::MI], bfr[2][CF::NI];
+    auto read_frags = [&](int buf, int kk, int f) {
+        const lds_char* sa = lds + buf * CF::A_BYTES;
+        const lds_char* sb = lds + buf * CF::B_BYTES;
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int chunk = 2 * kk + khalf;
-            bf16x8 af[TL::MI], bfr[TL::NI];
+        for (int i = 0; i < CF::MI; ++i)
+            af[f][i] = *(const __attribute__((address_space(3))) bf16x8*)(sa + a_off[kk] + i * 32 * 64);
 #pragma unroll
-            for (int i = 0; i < TL::MI; ++i) {
-                const U32x4 t = sa[lds_chunk(a_row0 + 32 * i, chunk)];
-                af[i] = __builtin_bit_cast(bf16x8, t);
-            }
-#pragma unroll
-            for (int j = 0; j < TL::NI; ++j) {
-                const U32x4 t = sb[lds_chunk(b_row0 + 32 * j, chunk)];
-                bfr[j] = __builtin_bit_cast(bf16x8, t);
-            }
-#pragma unroll
-            for (int i = 0; i < TL::MI; ++i)
-#pragma unroll
-                for (int j = 0; j < TL::NI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < CF::NI; ++j) {
+            const lds_char* p = sb + b_off[j] + kk * 16 * CF::B_ROW;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(p + 4 * CF::B_ROW));
+            typedef short i16x8 __attribute__((ext_vector_type(8)));
+            const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            bfr[f][j] = __builtin_bit_cast(bf16x8, both);
         }
-        if (ks + 1 < ksteps) store_stage(cur ^ 1);
-        __syncthreads();
+    };
+    auto mfma = [&](int f) {
+#pragma unroll
+        for (int i = 0; i < CF::MI; ++i)
+#pragma unroll
+            for (int j = 0; j < CF::NI; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f][i], bfr[f][j], acc[i][j], 0, 0, 0);
+    };
+
+    // ---- pipeline over stages of 32 k; DMA runs up to kStages stages ahead.
+    // Iteration s: fragments (s, 0) are in registers; read (s, 1); MFMAs of
+    // (s, 0); wait for stage s + 1's DMA and for this wave's LDS reads;
+    // barrier (stage s + 1 visible to every wave, every read of buffer s
+    // done); DMA stage s + 4 into buffer s; read (s + 1, 0); MFMAs of (s, 1).
+    const int nk = (int)(K / kBK);
+    // Every iteration issues one stage, so the vmcnt arithmetic is the same
+    // everywhere: past the last stage the source is clamped to stage nk - 1
+    // and lands in a buffer nobody reads again.
+    auto issue_clamped = [&](int st) { issue(st < nk ? st : nk - 1, st & (kStages - 1)); };
+#pragma unroll
+    for (int st = 0; st < kStages; ++st) issue_clamped(st);
+    wait_vmcnt<(kStages - 1) * CF::LOADS>();  // stage 0 landed
+    barrier();
+    read_frags(0, 0, 0);
+    for (int st = 0; st < nk; ++st) {
+        read_frags(st & (kStages - 1), 1, 1);
+        mfma(0);
+        wait_vmcnt<(kStages - 2) * CF::LOADS>();  // stage st + 1 landed (st + 2, st + 3 may be in flight)
+        wait_lgkmcnt0();                           // this wave's reads of buffer st are done
+        barrier();
+        issue_clamped(st + kStages);  // into buffer st, free since this barrier
+        read_frags((st + 1) & (kStages - 1), 0, 0);
+        mfma(1);
     }
+    wait_vmcnt<0>();  // no DMA may still target this workgroup's LDS at exit
 
     // Epilogue: lane holds column (lane & 31) of each 32 x 32 block, rows
     // 8 (v / 4) + 4 (lane / 32) + (v % 4).
     uint16_t* Cl = C + (int64_t)layer * M * N;
 #pragma unroll
-    for (int i = 0; i < TL::MI; ++i)
+    for (int i = 0; i < CF::MI; ++i)
 #pragma unroll
-        for (int j = 0; j < TL::NI; ++j) {
-            const int64_t col = n0 + wn * (BN / 2) + 32 * j + (lane & 31);
+        for (int j = 0; j < CF::NI; ++j) {
+            const int64_t col = n0 + wn * CF::WTN + 32 * j + (lane & 31);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t row = m0 + wm * (BM / 2) + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                const int64_t row = m0 + wm * CF::WTM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                 if (row < M) Cl[row * N + col] = (uint16_t)to_bf16(acc[i][j][v]);
             }
         }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN>
 int launch_tiles(const ProjectArgs& a, hipStream_t stream) {
-    using TL = Tile<BM, BN>;
+    using CF = Cfg<BM, BN, WM, WN>;
     const int tiles_m = (int)((a.M + BM - 1) / BM);
     const int tiles_n = (int)(a.N / BN);
     const int total = a.L * tiles_m * tiles_n;
-    const size_t lds_bytes = 2 * TL::STAGE_CHUNKS * sizeof(U32x4);
+    const size_t lds_bytes = CF::LDS_BYTES;
     if (lds_bytes > 65536) {
         // The opt-in above 64 KiB is per kernel and device; set it on each device once.
         static bool attr_set[64] = {};
@@ -217,14 +261,14 @@ int launch_tiles(const ProjectArgs& a, hipStream_t stream) {
         if (hipGetDevice(&dev) != hipSuccess) return -1;
         if (dev < 0 || dev >= 64) return -1;
         if (!attr_set[dev]) {
-            if (hipFuncSetAttribute((const void*)kv_project_kernel<BM, BN>,
+            if (hipFuncSetAttribute((const void*)kv_project_kernel<BM, BN, WM, WN>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) != hipSuccess)
                 return -1;
             attr_set[dev] = true;
         }
     }
-    hipLaunchKernelGGL((kv_project_kernel<BM, BN>), dim3(total), dim3(kThreads), lds_bytes, stream, a.A, a.B, a.C,
-                       a.M, a.K, a.N, tiles_m, tiles_n, total);
+    hipLaunchKernelGGL((kv_project_kernel<BM, BN, WM, WN>), dim3(total), dim3(CF::THREADS), lds_bytes, stream, a.A,
+                       a.B, a.C, a.M, a.K, a.N, tiles_m, tiles_n, total);
     return 0;
 }
 
@@ -236,9 +280,9 @@ int launch_kv_project(const ProjectArgs& a, hipStream_t stream) {
     const int cus = a.num_cus > 0 ? a.num_cus : 256;
     int rc;
     if (a.N % 256 == 0 && big_tiles >= cus)
-        rc = launch_tiles<256, 256>(a, stream);
+        rc = launch_tiles<256, 256, 2, 4>(a, stream);
     else
-        rc = launch_tiles<128, 128>(a, stream);
+        rc = launch_tiles<128, 128, 2, 2>(a, stream);
     if (rc) return rc;
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
