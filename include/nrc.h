@@ -136,6 +136,15 @@ int32_t nrc_context_kv_store(const uint16_t* k, const uint16_t* v, int64_t k_lay
  */
 int32_t nrc_check_scalars(const float* in, uint16_t* bf16_out, float* rsqrt_out, int64_t n, void* stream);
 
+/*
+ * nrc_check_bf16_pair - diagnostic: the paired hardware f32 -> bf16
+ * conversion (v_cvt_pk_bf16_f32) that nrc_context_norms uses on rows that
+ * cannot produce NaN, applied to n device floats: out[i] for in[i]. For
+ * every non-NaN input it must equal nrc_check_scalars' bf16 rounding.
+ * n <= 2^32. Errors: NRC_EINVAL.
+ */
+int32_t nrc_check_bf16_pair(const float* in, uint16_t* out, int64_t n, void* stream);
+
 /* Thread-local description of the last non-zero status of this thread. */
 const char* nrc_last_error(void);
 

@@ -23,6 +23,7 @@ __all__ = [
     "context_kv_chain",
     "kv_views",
     "check_scalars",
+    "check_bf16_pair",
     "library_path",
     "abi_version",
 ]
@@ -73,6 +74,8 @@ def _load():
         ctypes.POINTER(_vp), _i64, _i64, _i32, _i32, _f32, _vp]
     L.nrc_check_scalars.restype = _i32
     L.nrc_check_scalars.argtypes = [_vp, _vp, _vp, _i64, _vp]
+    L.nrc_check_bf16_pair.restype = _i32
+    L.nrc_check_bf16_pair.argtypes = [_vp, _vp, _i64, _vp]
     _lib = L
     return L
 
@@ -233,6 +236,18 @@ def check_scalars(x, want_bf16=True, want_rsqrt=True, stream=None):
     rs = torch.empty_like(x) if want_rsqrt else None
     _check(_load().nrc_check_scalars(_ptr(x), _ptr(bf), _ptr(rs), x.numel(), _stream(stream)))
     return bf, rs
+
+
+def check_bf16_pair(x, stream=None):
+    """Diagnostic: the paired hardware bf16 conversion the norms use on
+    NaN-free rows, applied to a float32 GPU tensor (bits as int16)."""
+    import torch
+
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float32 GPU tensor")
+    out = torch.empty(x.shape, dtype=torch.int16, device=x.device)
+    _check(_load().nrc_check_bf16_pair(_ptr(x), _ptr(out), x.numel(), _stream(stream)))
+    return out
 
 
 def context_kv_chain(x, hidden_w, pre_w, w_kv, positions, slots, cos_sin, caches, H, hidden_eps=1e-6,

@@ -182,4 +182,11 @@ int32_t nrc_check_scalars(const float* in, uint16_t* bf16_out, float* rsqrt_out,
     return launch_status(nrc::launch_scalars(in, bf16_out, rsqrt_out, n, (hipStream_t)stream), "check_scalars");
 }
 
+int32_t nrc_check_bf16_pair(const float* in, uint16_t* out, int64_t n, void* stream) {
+    if (n < 0 || n > ((int64_t)1 << 32)) return fail(NRC_EINVAL, "check_bf16_pair: n out of range");
+    if (n == 0) return NRC_OK;
+    if (!in || !out) return fail(NRC_EINVAL, "check_bf16_pair: NULL operand");
+    return launch_status(nrc::launch_bf16_pair(in, out, n, (hipStream_t)stream), "check_bf16_pair");
+}
+
 }  // extern "C"

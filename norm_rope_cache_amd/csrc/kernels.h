@@ -58,6 +58,7 @@ struct ProjectArgs {
 
 int launch_kv_project(const ProjectArgs& a, hipStream_t stream);
 
+int launch_bf16_pair(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
 int launch_scalars(const float* in, uint16_t* bf, float* rs, int64_t n, hipStream_t stream);
 
 }  // namespace nrc
