@@ -1,8 +1,11 @@
 """Throughput of the context K/V chain on one MI355X.
 
-One step = the whole hot path over one batch of synthetic context rows:
-context_norms -> context_kv_project -> context_kv_store (all three kernels,
-on one stream, inputs and outputs resident in HBM). The default workload is
+One step = the whole hot path over one batch of synthetic context rows, on
+one stream, inputs and outputs resident in HBM. Default path: context_norms ->
+context_kv_project -> context_kv_store. --path fused times
+context_hidden_norm (hidden norm + per-row layer-norm scale) ->
+context_kv_project_fused (layer norms applied while staging the projection's
+A tiles) -> context_kv_store instead. The default workload is
 the long-context configuration (L=4 draft layers, T=16384 rows, D=8192,
 H=8 KV heads, RoPE table [131072, 64], block size 16, 8192 blocks).
 
@@ -95,6 +98,7 @@ def main():
     ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--path", choices=("fused", "unfused"), default="unfused")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device-to-device once, a known-size reference for HBM byte counters")
     args = ap.parse_args()
@@ -131,17 +135,30 @@ def main():
     slots = dv(d["slots"])
     caches = torch.empty((cfg.L, cfg.num_blocks, cfg.H, cfg.block_size, 128), dtype=torch.bfloat16, device=dev)
     caches.view(torch.int16).random_(-32768, 32767)
-    normed = torch.empty((cfg.L, cfg.T, 8192), dtype=torch.bfloat16, device=dev)
+    fused = args.path == "fused"
+    if fused:
+        h = torch.empty((cfg.T, 8192), dtype=torch.bfloat16, device=dev)
+        r = torch.empty((cfg.T,), dtype=torch.float32, device=dev)
+    else:
+        normed = torch.empty((cfg.L, cfg.T, 8192), dtype=torch.bfloat16, device=dev)
     kv = torch.empty((cfg.L, cfg.T, cfg.N), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
+    names = (["context_hidden_norm", "context_kv_project_fused", "context_kv_store"] if fused else
+             ["context_norms", "context_kv_project", "context_kv_store"])
 
     def step(ev=None):
         if ev:
             ev[0].record()
-        nrc.context_norms(x, hw, pw, cfg.L, d["hidden_eps"], d["pre_eps"], out=normed)
+        if fused:
+            nrc.context_hidden_norm(x, hw, pw, cfg.L, d["hidden_eps"], d["pre_eps"], h=h, r=r)
+        else:
+            nrc.context_norms(x, hw, pw, cfg.L, d["hidden_eps"], d["pre_eps"], out=normed)
         if ev:
             ev[1].record()
-        nrc.context_kv_project(normed, w_kv, out=kv)
+        if fused:
+            nrc.context_kv_project_fused(h, r, pw, w_kv, out=kv)
+        else:
+            nrc.context_kv_project(normed, w_kv, out=kv)
         if ev:
             ev[2].record()
         nrc.context_kv_store(kv, positions, slots, cos_sin, caches, cfg.H, d["k_eps"])
@@ -171,22 +188,22 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    k_ms = {"context_norms": [], "context_kv_project": [], "context_kv_store": []}
+    k_ms = {n: [] for n in names}
     for ev in events:
-        k_ms["context_norms"].append(ev[0].elapsed_time(ev[1]))
-        k_ms["context_kv_project"].append(ev[1].elapsed_time(ev[2]))
-        k_ms["context_kv_store"].append(ev[2].elapsed_time(ev[3]))
+        for i, n in enumerate(names):
+            k_ms[n].append(ev[i].elapsed_time(ev[i + 1]))
     avg = {k: sum(v) / len(v) for k, v in k_ms.items()}
     log("per-kernel ms: " + ", ".join(f"{k}={v:.4f}" for k, v in avg.items()) + f"; wall/step {ms_step:.4f}")
 
     norms_b, store_b, flops = algorithmic_bytes(cfg, d["slots"])
+    n0, n1, n2 = names
+    if fused:
+        # pre-pass: read x, write h and r (plus the hidden weight once)
+        norms_b = cfg.T * (2 * 8192 + 2 * 8192 + 4) + (2 * 8192 if cfg.hidden_weighted else 0)
     kernels = {
-        "context_norms": {"bound": "hbm", "ms": avg["context_norms"], "bytes": norms_b,
-                          "achieved_GBs": norms_b / (avg["context_norms"] * 1e-3) / 1e9},
-        "context_kv_project": {"bound": "mfma", "ms": avg["context_kv_project"], "flops": flops,
-                               "achieved_TFLOPs": flops / (avg["context_kv_project"] * 1e-3) / 1e12},
-        "context_kv_store": {"bound": "hbm", "ms": avg["context_kv_store"], "bytes": store_b,
-                             "achieved_GBs": store_b / (avg["context_kv_store"] * 1e-3) / 1e9},
+        n0: {"bound": "hbm", "ms": avg[n0], "bytes": norms_b, "achieved_GBs": norms_b / (avg[n0] * 1e-3) / 1e9},
+        n1: {"bound": "mfma", "ms": avg[n1], "flops": flops, "achieved_TFLOPs": flops / (avg[n1] * 1e-3) / 1e12},
+        n2: {"bound": "hbm", "ms": avg[n2], "bytes": store_b, "achieved_GBs": store_b / (avg[n2] * 1e-3) / 1e9},
     }
     for k, rec in kernels.items():
         if rec["bound"] == "hbm":
@@ -238,6 +255,7 @@ def main():
             "global_batch": cfg.T,
             "seq_len": cfg.T,
             "parallelism": "single GPU",
+            "path": args.path,
         },
         "roofline": roofline,
         "kernels": kernels,

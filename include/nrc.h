@@ -87,6 +87,45 @@ int32_t nrc_context_kv_project(const uint16_t* normed, const uint16_t* w, uint16
                                int64_t D, int64_t N, void* stream);
 
 /*
+ * nrc_context_hidden_norm - the pre-pass of the fused norms + projection: the
+ * hidden norm and each row's layer-norm scale, the two quantities every
+ * layer norm of a row shares. Page "...cutedsl.draft.context", ContextNorms
+ * (the hidden norm's output is rounded to bf16 before the layer norms read
+ * it; the layer norms share eps and center, page "...runtime.draft",
+ * _context_norm_constants).
+ *
+ *   x, T, D, hidden_w, hidden_eps, hidden_center: as nrc_context_norms.
+ *   pre_w [L, D] or NULL, pre_eps, pre_center: the layer norms' operands (the
+ *          weights are only checked for finiteness here).
+ *   h  [T, D] bf16, 16-byte aligned: the hidden norm's bf16 output.
+ *   r  [T] float: 1/sqrt(S_p/8192 + pre_eps), S_p the row's sum of squares
+ *      of h in the library's order. The sign bit is set on rows whose layer
+ *      outputs may be NaN (non-finite S_p or scale, non-finite layer weights
+ *      or center); |r| is the scale.
+ * nrc_context_norms' output equals bf16((h * |r|) * (pre_w[l] + pre_center))
+ * element by element. Errors as nrc_context_norms.
+ */
+int32_t nrc_context_hidden_norm(const uint16_t* x, int64_t T, int64_t D, const uint16_t* hidden_w,
+                                const uint16_t* pre_w, int32_t L, float hidden_eps, float pre_eps,
+                                float hidden_center, float pre_center, uint16_t* h, float* r, void* stream);
+
+/*
+ * nrc_context_kv_project_fused - the projection with the layer norms applied
+ * on the fly: kv[l] = A_l . w[l], A_l = bf16((h * |r|) * (pre_w[l] +
+ * pre_center)) (no weight: bf16(h * |r|)). Bit-identical to
+ * nrc_context_norms followed by nrc_context_kv_project, without the
+ * [L, T, D] intermediate. Page "...runtime.draft", ContextKV._project.
+ *
+ *   h [T, D] bf16 and r [T] from nrc_context_hidden_norm; pre_w [L, D] bf16
+ *   or NULL; w [L, D, N]; kv [L, T, N] as nrc_context_kv_project. D = 8192.
+ * Errors: NRC_EINVAL (NULLs, L < 1, T < 0, misalignment), NRC_ENOTSUP
+ * (D != 8192, N not a positive multiple of 128).
+ */
+int32_t nrc_context_kv_project_fused(const uint16_t* h, const float* r, const uint16_t* pre_w, float pre_center,
+                                     const uint16_t* w, uint16_t* kv, int32_t L, int64_t T, int64_t D, int64_t N,
+                                     void* stream);
+
+/*
  * nrc_context_kv_store - weightless K-norm, GPT-J RoPE and paged-cache insert
  * of L layers. Page "...cutedsl.draft.context", sections ContextKvStore,
  * _ContextKvStoreKernel, _sum_squares_64 and _rope; operand checks per

@@ -9,7 +9,9 @@ libnrc.so is missing, every call raises.
     context_norms(x, hidden_w, pre_w, L, ...)      -> [L, T, 8192] bf16
     context_kv_project(normed, w_kv)               -> [L, T, N] bf16
     context_kv_store(kv, positions, slots, cos_sin, caches, H, ...)   (in place)
-    context_kv_chain(...)                          all three in order
+    context_hidden_norm(x, ...) -> (h, r)          pre-pass of the fused path
+    context_kv_project_fused(h, r, pre_w, w_kv)    projection with the layer norms fused in
+    context_kv_chain(...)                          the whole chain (fused by default)
 """
 
 import ctypes
@@ -21,6 +23,8 @@ __all__ = [
     "context_kv_project",
     "context_kv_store",
     "context_kv_chain",
+    "context_hidden_norm",
+    "context_kv_project_fused",
     "kv_views",
     "check_scalars",
     "check_bf16_pair",
@@ -72,6 +76,10 @@ def _load():
     L.nrc_context_kv_store.argtypes = [
         _vp, _vp, _i64, _i64, _i64, _i64, _vp, ctypes.POINTER(_vp), _i64, _i64, _vp, _i64,
         ctypes.POINTER(_vp), _i64, _i64, _i32, _i32, _f32, _vp]
+    L.nrc_context_hidden_norm.restype = _i32
+    L.nrc_context_hidden_norm.argtypes = [_vp, _i64, _i64, _vp, _vp, _i32, _f32, _f32, _f32, _f32, _vp, _vp, _vp]
+    L.nrc_context_kv_project_fused.restype = _i32
+    L.nrc_context_kv_project_fused.argtypes = [_vp, _vp, _vp, _f32, _vp, _vp, _i32, _i64, _i64, _i64, _vp]
     L.nrc_check_scalars.restype = _i32
     L.nrc_check_scalars.argtypes = [_vp, _vp, _vp, _i64, _vp]
     L.nrc_check_bf16_pair.restype = _i32
@@ -140,6 +148,59 @@ def context_norms(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hidden_c
             raise ValueError("out must be [L, T, D]")
     _check(_load().nrc_context_norms(_ptr(x), T, D, _ptr(hidden_w), _ptr(pre_w), L, hidden_eps, pre_eps,
                                      hidden_center, pre_center, _ptr(out), _stream(stream)))
+    return out
+
+
+def context_hidden_norm(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hidden_center=0.0, pre_center=0.0,
+                        h=None, r=None, stream=None):
+    """Pre-pass of the fused path: (h [T, 8192] bf16, r [T] float32)."""
+    import torch
+
+    _bf16(x, "x")
+    T, D = x.shape
+    if hidden_w is not None:
+        _bf16(hidden_w, "hidden_w")
+    if pre_w is not None:
+        _bf16(pre_w, "pre_w")
+        if tuple(pre_w.shape) != (L, D):
+            raise ValueError("pre_w must be [L, D]")
+    if h is None:
+        h = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+    if r is None:
+        r = torch.empty((T,), dtype=torch.float32, device=x.device)
+    _bf16(h, "h")
+    if tuple(h.shape) != (T, D) or r.dtype != torch.float32 or tuple(r.shape) != (T,) or not r.is_contiguous():
+        raise ValueError("h must be [T, D] bf16 and r [T] float32")
+    _check(_load().nrc_context_hidden_norm(_ptr(x), T, D, _ptr(hidden_w), _ptr(pre_w), L, hidden_eps, pre_eps,
+                                           hidden_center, pre_center, _ptr(h), _ptr(r), _stream(stream)))
+    return h, r
+
+
+def context_kv_project_fused(h, r, pre_w, w_kv, pre_center=0.0, out=None, stream=None):
+    """kv[l] = bf16((h * |r|) * (pre_w[l] + pre_center)) . w_kv[l]; equal to
+    context_norms followed by context_kv_project."""
+    import torch
+
+    _bf16(h, "h")
+    _bf16(w_kv, "w_kv")
+    T, D = h.shape
+    L, Dw, N = w_kv.shape
+    if Dw != D:
+        raise ValueError("w_kv must be [L, D, N]")
+    if pre_w is not None:
+        _bf16(pre_w, "pre_w")
+        if tuple(pre_w.shape) != (L, D):
+            raise ValueError("pre_w must be [L, D]")
+    if r.dtype != torch.float32 or tuple(r.shape) != (T,) or not r.is_contiguous():
+        raise ValueError("r must be a contiguous float32 [T]")
+    if out is None:
+        out = torch.empty((L, T, N), dtype=torch.bfloat16, device=h.device)
+    else:
+        _bf16(out, "out")
+        if tuple(out.shape) != (L, T, N):
+            raise ValueError("out must be [L, T, N]")
+    _check(_load().nrc_context_kv_project_fused(_ptr(h), _ptr(r), _ptr(pre_w), pre_center, _ptr(w_kv), _ptr(out), L,
+                                                T, D, N, _stream(stream)))
     return out
 
 
@@ -251,12 +312,19 @@ def check_bf16_pair(x, stream=None):
 
 
 def context_kv_chain(x, hidden_w, pre_w, w_kv, positions, slots, cos_sin, caches, H, hidden_eps=1e-6,
-                     pre_eps=1e-6, k_eps=1e-6, normed=None, kv=None, stream=None):
-    """The whole chain: norms -> projection -> K-norm/RoPE/insert. `normed`
-    [L, T, 8192] and `kv` [L, T, N] may be passed in as preallocated
-    intermediates. Returns (normed, kv)."""
+                     pre_eps=1e-6, k_eps=1e-6, fused=True, workspace=None, kv=None, stream=None):
+    """The whole chain, in place on `caches`; returns kv [L, T, N].
+
+    fused=True: pre-pass (h, r) -> fused projection -> store; `workspace` may
+    be a tuple (h [T, 8192] bf16, r [T] float32). fused=False: norms into
+    `workspace` ([L, T, 8192] bf16) -> projection -> store."""
     L = w_kv.shape[0]
-    normed = context_norms(x, hidden_w, pre_w, L, hidden_eps, pre_eps, out=normed, stream=stream)
-    kv = context_kv_project(normed, w_kv, out=kv, stream=stream)
+    if fused:
+        h, r = workspace if workspace is not None else (None, None)
+        h, r = context_hidden_norm(x, hidden_w, pre_w, L, hidden_eps, pre_eps, h=h, r=r, stream=stream)
+        kv = context_kv_project_fused(h, r, pre_w, w_kv, out=kv, stream=stream)
+    else:
+        normed = context_norms(x, hidden_w, pre_w, L, hidden_eps, pre_eps, out=workspace, stream=stream)
+        kv = context_kv_project(normed, w_kv, out=kv, stream=stream)
     context_kv_store(kv, positions, slots, cos_sin, caches, H, k_eps, stream=stream)
-    return normed, kv
+    return kv

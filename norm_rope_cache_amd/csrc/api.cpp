@@ -75,6 +75,43 @@ int32_t nrc_context_norms(const uint16_t* x, int64_t T, int64_t D, const uint16_
     return launch_status(nrc::launch_context_norms(a, (hipStream_t)stream), "context_norms");
 }
 
+int32_t nrc_context_hidden_norm(const uint16_t* x, int64_t T, int64_t D, const uint16_t* hidden_w,
+                                const uint16_t* pre_w, int32_t L, float hidden_eps, float pre_eps,
+                                float hidden_center, float pre_center, uint16_t* h, float* r, void* stream) {
+    if (D != NRC_HIDDEN) return fail(NRC_ENOTSUP, "context_hidden_norm: rows of %lld, not %d", (long long)D, NRC_HIDDEN);
+    if (T < 0) return fail(NRC_EINVAL, "context_hidden_norm: T = %lld < 0", (long long)T);
+    if (L < 1) return fail(NRC_EINVAL, "context_hidden_norm: L = %d < 1", L);
+    if (T > ((int64_t)1 << 40) / D) return fail(NRC_EINVAL, "context_hidden_norm: T too large");
+    if (T == 0) return NRC_OK;
+    if (!x || !h || !r) return fail(NRC_EINVAL, "context_hidden_norm: NULL x, h or r");
+    if (!aligned(x, 16) || !aligned(h, 16) || !aligned(r, 4) || (hidden_w && !aligned(hidden_w, 16)) ||
+        (pre_w && !aligned(pre_w, 16)))
+        return fail(NRC_EINVAL, "context_hidden_norm: operands must be 16-byte aligned (r 4-byte)");
+    nrc::NormsArgs a{x, T, hidden_w, pre_w, L, hidden_eps, pre_eps, hidden_center, pre_center, nullptr, num_cus()};
+    return launch_status(nrc::launch_hidden_norm(a, h, r, (hipStream_t)stream), "context_hidden_norm");
+}
+
+int32_t nrc_context_kv_project_fused(const uint16_t* h, const float* r, const uint16_t* pre_w, float pre_center,
+                                     const uint16_t* w, uint16_t* kv, int32_t L, int64_t T, int64_t D, int64_t N,
+                                     void* stream) {
+    if (L < 1) return fail(NRC_EINVAL, "context_kv_project_fused: L = %d < 1", L);
+    if (T < 0) return fail(NRC_EINVAL, "context_kv_project_fused: T = %lld < 0", (long long)T);
+    if (D != NRC_HIDDEN)
+        return fail(NRC_ENOTSUP, "context_kv_project_fused: rows of %lld, not %d", (long long)D, NRC_HIDDEN);
+    if (N <= 0 || N % 128)
+        return fail(NRC_ENOTSUP, "context_kv_project_fused: N = %lld is not a positive multiple of 128 (2 H 64)",
+                    (long long)N);
+    if (T > ((int64_t)1 << 31) || N > ((int64_t)1 << 20) || (int64_t)L * ((T + 127) / 128) * (N / 128) > ((int64_t)1 << 30))
+        return fail(NRC_EINVAL, "context_kv_project_fused: shape too large");
+    if (T == 0) return NRC_OK;
+    if (!h || !r || !w || !kv) return fail(NRC_EINVAL, "context_kv_project_fused: NULL operand");
+    if (!aligned(h, 16) || !aligned(w, 16) || !aligned(kv, 16) || !aligned(r, 4) || (pre_w && !aligned(pre_w, 16)))
+        return fail(NRC_EINVAL, "context_kv_project_fused: operands must be 16-byte aligned (r 4-byte)");
+    nrc::ProjectArgs a{h, w, kv, L, T, D, N, num_cus()};
+    return launch_status(nrc::launch_kv_project_fused(a, r, pre_w, pre_center, (hipStream_t)stream),
+                         "context_kv_project_fused");
+}
+
 int32_t nrc_context_kv_project(const uint16_t* normed, const uint16_t* w, uint16_t* kv, int32_t L, int64_t T,
                                int64_t D, int64_t N, void* stream) {
     if (L < 1) return fail(NRC_EINVAL, "context_kv_project: L = %d < 1", L);

@@ -108,11 +108,18 @@ constexpr int kRowBytes = kHidden * 2;     // 16 KiB of bf16 weights per norm
 // centers are +-0.0 and the add is folded into the staged weights (a -0.0
 // weight turns into +0.0 when its center is +0.0, the only case where
 // w + center differs from w).
-template <bool WEIGHTS_IN_LDS, bool HW, bool PW, bool ADD_CENTER>
+//
+// PREPASS: instead of the L layer outputs, write the two per-row quantities
+// the layer norms share - h_out [T, 8192], the hidden norm's bf16 output, and
+// r_out [T], the layer-norm scale 1/sqrt(S_p/8192 + eps) - for a projection
+// that applies the layer weights itself. r_out's sign bit marks a row whose
+// layer outputs may be NaN (non-finite sum or scale, or a non-finite layer
+// weight or center), which must take the exact bf16 rounding.
+template <bool WEIGHTS_IN_LDS, bool HW, bool PW, bool ADD_CENTER, bool PREPASS>
 __global__ __launch_bounds__(kBlockThreads) void context_norms_kernel(
     const uint16_t* __restrict__ x, int64_t T, const uint16_t* __restrict__ hidden_w,
     const uint16_t* __restrict__ pre_w, int32_t L, float hidden_eps, float pre_eps, float hidden_center,
-    float pre_center, uint16_t* __restrict__ out) {
+    float pre_center, uint16_t* __restrict__ out, uint16_t* __restrict__ h_out, float* __restrict__ r_out) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ float sums[kSlots][2][4];
     const int tid = threadIdx.x;
@@ -140,11 +147,21 @@ __global__ __launch_bounds__(kBlockThreads) void context_norms_kernel(
         wfinite = wfinite && finite8(w);
         wl[c] = w;
     }
+    bool pfinite = true;  // layer weights (and center) finite
     if constexpr (PW && !WEIGHTS_IN_LDS) {
-        for (int c = tid; c < L * (kRowBytes / 16); c += kBlockThreads) wfinite = wfinite && finite8(load16(pre_w + 8 * c));
+        for (int c = tid; c < L * (kRowBytes / 16); c += kBlockThreads) pfinite = pfinite && finite8(load16(pre_w + 8 * c));
     }
-    if constexpr (ADD_CENTER) wfinite = wfinite && finite(hidden_center) && finite(pre_center);
-    wfinite = __syncthreads_and(wfinite) != 0;
+    if constexpr (ADD_CENTER) {
+        wfinite = wfinite && finite(hidden_center);
+        pfinite = pfinite && finite(pre_center);
+    }
+    if constexpr (PREPASS) {
+        // the hidden conversion needs only the hidden weights finite
+        wfinite = __syncthreads_and(wfinite) != 0;
+        pfinite = __syncthreads_and(pfinite) != 0;
+    } else {
+        wfinite = __syncthreads_and(wfinite && pfinite) != 0;
+    }
     const U32x4* gh = wl + (col0 >> 3);                    // chunk (col0 + 2048 k) / 8
     const U32x4* gp = wl + hw_chunks + (col0 >> 3);
 
@@ -213,6 +230,24 @@ __global__ __launch_bounds__(kBlockThreads) void context_norms_kernel(
         // center, and the weight applies after the norm).
         const float Sp = row_sum(lane_sumsq(u), sums[slot][1]);
         const float rp = rsqrt_rn(__builtin_fmaf(Sp, 0x1p-13f, pre_eps));
+        if constexpr (PREPASS) {
+            if (active) {
+                uint16_t* o = h_out + row * kHidden + col0;
+#pragma unroll
+                for (int k = 0; k < kFrags; ++k) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        w[p] = (__float_as_uint(u[k][2 * p]) >> 16) | (__float_as_uint(u[k][2 * p + 1]) & 0xFFFF0000u);
+                    store16(o + k * kChunk, U32x4{w[0], w[1], w[2], w[3]});
+                }
+                if (t == 0) {
+                    const bool ok = pfinite && finite(Sp) && finite(rp);
+                    r_out[row] = ok ? rp : __uint_as_float(__float_as_uint(rp) | 0x80000000u);
+                }
+            }
+            continue;
+        }
         const bool fast_p = fast_h && finite(Sp) && finite(rp);
 #pragma unroll
         for (int k = 0; k < kFrags; ++k)
@@ -261,13 +296,13 @@ __global__ __launch_bounds__(kBlockThreads) void context_norms_kernel(
     }
 }
 
-template <bool WEIGHTS_IN_LDS, bool ADD_CENTER>
-void launch_w(const NormsArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
+template <bool WEIGHTS_IN_LDS, bool ADD_CENTER, bool PREPASS>
+void launch_w(const NormsArgs& a, dim3 grid, size_t lds, uint16_t* h_out, float* r_out, hipStream_t stream) {
     const bool hw = a.hidden_w != nullptr, pw = a.pre_w != nullptr;
-#define NRC_NORMS_LAUNCH(H, P)                                                                                 \
-    hipLaunchKernelGGL((context_norms_kernel<WEIGHTS_IN_LDS, H, P, ADD_CENTER>), grid, dim3(kBlockThreads), lds, \
-                       stream, a.x, a.T, a.hidden_w, a.pre_w, a.L, a.hidden_eps, a.pre_eps, a.hidden_center,     \
-                       a.pre_center, a.out)
+#define NRC_NORMS_LAUNCH(H, P)                                                                                \
+    hipLaunchKernelGGL((context_norms_kernel<WEIGHTS_IN_LDS, H, P, ADD_CENTER, PREPASS>), grid,                 \
+                       dim3(kBlockThreads), lds, stream, a.x, a.T, a.hidden_w, a.pre_w, a.L, a.hidden_eps,      \
+                       a.pre_eps, a.hidden_center, a.pre_center, a.out, h_out, r_out)
     if (hw && pw)
         NRC_NORMS_LAUNCH(true, true);
     else if (hw)
@@ -279,16 +314,16 @@ void launch_w(const NormsArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
 #undef NRC_NORMS_LAUNCH
 }
 
-template <bool WEIGHTS_IN_LDS, bool ADD_CENTER>
+template <bool WEIGHTS_IN_LDS, bool ADD_CENTER, bool PREPASS>
 int set_lds_limit() {
     // The opt-in above 64 KiB of LDS is per kernel and device.
     static bool done[64][4] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-    const void* fns[4] = {(const void*)context_norms_kernel<WEIGHTS_IN_LDS, true, true, ADD_CENTER>,
-                          (const void*)context_norms_kernel<WEIGHTS_IN_LDS, true, false, ADD_CENTER>,
-                          (const void*)context_norms_kernel<WEIGHTS_IN_LDS, false, true, ADD_CENTER>,
-                          (const void*)context_norms_kernel<WEIGHTS_IN_LDS, false, false, ADD_CENTER>};
+    const void* fns[4] = {(const void*)context_norms_kernel<WEIGHTS_IN_LDS, true, true, ADD_CENTER, PREPASS>,
+                          (const void*)context_norms_kernel<WEIGHTS_IN_LDS, true, false, ADD_CENTER, PREPASS>,
+                          (const void*)context_norms_kernel<WEIGHTS_IN_LDS, false, true, ADD_CENTER, PREPASS>,
+                          (const void*)context_norms_kernel<WEIGHTS_IN_LDS, false, false, ADD_CENTER, PREPASS>};
     for (int i = 0; i < 4; ++i) {
         if (done[dev][i]) continue;
         if (hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, 9 * kRowBytes) != hipSuccess)
@@ -298,34 +333,49 @@ int set_lds_limit() {
     return 0;
 }
 
-}  // namespace
-
-int launch_context_norms(const NormsArgs& a, hipStream_t stream) {
-    const bool in_lds = a.L <= 8;
-    const size_t lds = (size_t)((a.hidden_w ? 1 : 0) + (a.pre_w && in_lds ? a.L : 0)) * kRowBytes;
+dim3 norms_grid(const NormsArgs& a, size_t lds) {
     // Workgroups resident per CU: LDS (160 KiB) and the 1024-thread size allow
     // one or two; rows beyond the grid are walked with a grid stride.
     const int64_t per_cu = lds <= 64 * 1024 ? 2 : 1;
     const int64_t groups = (a.T + kSlots - 1) / kSlots;
     const int64_t max_blocks = (int64_t)(a.num_cus > 0 ? a.num_cus : 256) * per_cu;
-    const dim3 grid((unsigned)(groups < max_blocks ? groups : max_blocks));
+    return dim3((unsigned)(groups < max_blocks ? groups : max_blocks));
+}
+
+}  // namespace
+
+int launch_context_norms(const NormsArgs& a, hipStream_t stream) {
+    const bool in_lds = a.L <= 8;
+    const size_t lds = (size_t)((a.hidden_w ? 1 : 0) + (a.pre_w && in_lds ? a.L : 0)) * kRowBytes;
+    const dim3 grid = norms_grid(a, lds);
     // A center of exactly +0.0 or -0.0 folds into the bf16 weights.
     const bool zero_centers = a.hidden_center == 0.0f && a.pre_center == 0.0f;
     int rc;
     if (in_lds) {
         if (zero_centers) {
-            if ((rc = set_lds_limit<true, false>())) return rc;
-            launch_w<true, false>(a, grid, lds, stream);
+            if ((rc = set_lds_limit<true, false, false>())) return rc;
+            launch_w<true, false, false>(a, grid, lds, nullptr, nullptr, stream);
         } else {
-            if ((rc = set_lds_limit<true, true>())) return rc;
-            launch_w<true, true>(a, grid, lds, stream);
+            if ((rc = set_lds_limit<true, true, false>())) return rc;
+            launch_w<true, true, false>(a, grid, lds, nullptr, nullptr, stream);
         }
     } else {
         if (zero_centers)
-            launch_w<false, false>(a, grid, lds, stream);
+            launch_w<false, false, false>(a, grid, lds, nullptr, nullptr, stream);
         else
-            launch_w<false, true>(a, grid, lds, stream);
+            launch_w<false, true, false>(a, grid, lds, nullptr, nullptr, stream);
     }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_hidden_norm(const NormsArgs& a, uint16_t* h_out, float* r_out, hipStream_t stream) {
+    const size_t lds = (size_t)(a.hidden_w ? 1 : 0) * kRowBytes;
+    const dim3 grid = norms_grid(a, lds);
+    const bool zero_centers = a.hidden_center == 0.0f && a.pre_center == 0.0f;
+    if (zero_centers)
+        launch_w<false, false, true>(a, grid, lds, h_out, r_out, stream);
+    else
+        launch_w<false, true, true>(a, grid, lds, h_out, r_out, stream);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

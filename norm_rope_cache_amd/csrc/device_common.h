@@ -72,6 +72,26 @@ struct alignas(16) U32x4 {
     uint32_t x, y, z, w;
 };
 
+// Two f32 -> packed bf16 with one v_cvt_pk_bf16_f32 (round to nearest even,
+// subnormals kept). Only for values that cannot be NaN: the hardware's NaN
+// encoding is not 0x7FC0 (pack_bf16 handles those).
+typedef float nrc_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 nrc_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16_pair_hw(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((nrc_f32x2){lo, hi}, nrc_bf16x2));
+}
+
+// (w + 0.0) on packed bf16 weights: a -0.0 weight becomes +0.0, all others
+// are unchanged.
+__device__ __forceinline__ uint32_t plus_zero_pair16(uint32_t w) {
+    if ((w & 0xFFFFu) == 0x8000u) w &= 0xFFFF0000u;
+    if ((w >> 16) == 0x8000u) w &= 0x0000FFFFu;
+    return w;
+}
+__device__ __forceinline__ U32x4 plus_zero16(U32x4 w) {
+    return U32x4{plus_zero_pair16(w.x), plus_zero_pair16(w.y), plus_zero_pair16(w.z), plus_zero_pair16(w.w)};
+}
+
 __device__ __forceinline__ U32x4 load16(const void* p) {
     return *reinterpret_cast<const U32x4*>(p);
 }

@@ -46,6 +46,8 @@ struct NormsArgs {
 };
 
 int launch_context_norms(const NormsArgs& a, hipStream_t stream);
+// h_out [T, 8192] bf16 and r_out [T]: the pre-pass of the fused projection (a.out unused).
+int launch_hidden_norm(const NormsArgs& a, uint16_t* h_out, float* r_out, hipStream_t stream);
 
 struct ProjectArgs {
     const uint16_t* A;  // [L, M, K]
@@ -57,6 +59,9 @@ struct ProjectArgs {
 };
 
 int launch_kv_project(const ProjectArgs& a, hipStream_t stream);
+// A = bf16((h * |r[m]|) * (gamma_l + center)) built in the kernel; a.A is h [M, K].
+int launch_kv_project_fused(const ProjectArgs& a, const float* r, const uint16_t* gamma, float center,
+                            hipStream_t stream);
 
 int launch_bf16_pair(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
 int launch_scalars(const float* in, uint16_t* bf, float* rs, int64_t n, hipStream_t stream);

@@ -32,6 +32,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) char lds_char;
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4v lds_u32x4;
 
 constexpr int kBK = 32;     // K per LDS stage
 constexpr int kStages = 4;  // LDS ring depth
@@ -76,12 +78,27 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
 }
 
-template <int BM, int BN, int WM, int WN>
+// A operand of the fused form: the layer-norm output built on the fly from
+// the hidden norm's bf16 output h [M, K], each row's scale r[m] (sign bit
+// set: the row may produce NaN and takes the exact bf16 rounding) and the
+// layer's weight gamma [L, K] (nullptr: weightless).
+struct FusedA {
+    const float* r;
+    const uint16_t* gamma;
+    float center;
+};
+
+// FUSED: false - A is the stacked layer-norm output [L, M, K] (tiles ordered
+// layer, M tile, N tile); true - A is built from FusedA (tiles ordered M
+// tile, layer, N tile, so the layers of one h panel run together).
+// CMODE (fused, with weights): 0 - gamma = w; 1 - gamma = w with -0.0 turned
+// into +0.0 (a +0.0 center); 2 - gamma = w + center in FP32.
+template <int BM, int BN, int WM, int WN, bool FUSED, bool PW, int CMODE>
 __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t* __restrict__ A,
                                                               const uint16_t* __restrict__ B,
                                                               uint16_t* __restrict__ C, int64_t M, int64_t K,
-                                                              int64_t N, int32_t tiles_m, int32_t tiles_n,
-                                                              int32_t total_tiles) {
+                                                              int64_t N, int32_t L, int32_t tiles_m, int32_t tiles_n,
+                                                              int32_t total_tiles, FusedA fa) {
     using CF = Cfg<BM, BN, WM, WN>;
     extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
     lds_char* lds = (lds_char*)lds_raw;
@@ -92,11 +109,17 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     int tile = blockIdx.x;
     if ((total_tiles & 7) == 0) tile = (blockIdx.x & 7) * (total_tiles >> 3) + (blockIdx.x >> 3);
     const int tn = tile % tiles_n;
-    const int tm = (tile / tiles_n) % tiles_m;
-    const int layer = tile / (tiles_n * tiles_m);
+    int tm, layer;
+    if constexpr (FUSED) {
+        layer = (tile / tiles_n) % L;
+        tm = tile / (tiles_n * L);
+    } else {
+        tm = (tile / tiles_n) % tiles_m;
+        layer = tile / (tiles_n * tiles_m);
+    }
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
-    const uint16_t* Al = A + (int64_t)layer * M * K;
+    const uint16_t* Al = FUSED ? A : A + (int64_t)layer * M * K;
     const uint16_t* Bl = B + (int64_t)layer * K * N;
 
     const int tid = threadIdx.x;
@@ -141,6 +164,65 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
         for (int t = 0; t < CF::B_LOADS; ++t)
             dma16(b_src[t] + kb, __builtin_amdgcn_readfirstlane(base + CF::A_REGION + buf * CF::B_BYTES +
                                                                 (wave * CF::B_LOADS + t) * 1024));
+    };
+
+    // ---- fused form: the layer weights of this tile sit in LDS past the
+    // ring; each lane rebuilds, in place, the A chunks its own DMA wrote:
+    // a = bf16((h * r) * gamma) per element (paired hardware conversion on
+    // rows flagged NaN-free, the exact rounding otherwise).
+    constexpr int G_OFF = CF::LDS_BYTES;
+    float a_r[CF::A_LOADS];
+    bool a_slow[CF::A_LOADS];
+    int a_kc[CF::A_LOADS];
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int t = 0; t < CF::A_LOADS; ++t) {
+            const int off = (wave * CF::A_LOADS + t) * 1024 + lane * 16;
+            const int r = off >> 6, pc = (off >> 4) & 3;
+            a_kc[t] = 8 * (pc ^ ((r >> 1) & 3));
+            int64_t row = m0 + r;
+            row = row < M ? row : M - 1;
+            const float rv = fa.r[row];
+            a_slow[t] = __builtin_signbit(rv);
+            a_r[t] = __builtin_fabsf(rv);
+        }
+        if constexpr (PW) {
+            const uint16_t* g = fa.gamma + (int64_t)layer * K;
+            for (int c = tid; c < (int)(K / 8); c += CF::THREADS) {
+                U32x4 w = load16(g + 8 * c);
+                if constexpr (CMODE == 1) w = plus_zero16(w);
+                *(lds_u32x4*)(lds + G_OFF + 16 * c) = u32x4v{w.x, w.y, w.z, w.w};
+            }
+        }
+        __syncthreads();  // the weights are visible before the first transform
+    }
+    auto transform = [&](int st, int buf) {
+        const int sk = st < (int)(K / kBK) ? st : (int)(K / kBK) - 1;
+#pragma unroll
+        for (int t = 0; t < CF::A_LOADS; ++t) {
+            lds_u32x4* p = (lds_u32x4*)(lds + buf * CF::A_BYTES + (wave * CF::A_LOADS + t) * 1024 + lane * 16);
+            const u32x4v hv = *p;
+            float y[8] = {bf16_lo(hv.x), bf16_hi(hv.x), bf16_lo(hv.y), bf16_hi(hv.y),
+                          bf16_lo(hv.z), bf16_hi(hv.z), bf16_lo(hv.w), bf16_hi(hv.w)};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = y[e] * a_r[t];
+            if constexpr (PW) {
+                const u32x4v gv = *(const lds_u32x4*)(lds + G_OFF + 2 * (sk * kBK + a_kc[t]));
+                float g[8] = {bf16_lo(gv.x), bf16_hi(gv.x), bf16_lo(gv.y), bf16_hi(gv.y),
+                              bf16_lo(gv.z), bf16_hi(gv.z), bf16_lo(gv.w), bf16_hi(gv.w)};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = y[e] * (CMODE == 2 ? g[e] + fa.center : g[e]);
+            }
+            u32x4v o;
+            if (!a_slow[t]) {
+                o = u32x4v{pack_bf16_pair_hw(y[0], y[1]), pack_bf16_pair_hw(y[2], y[3]),
+                           pack_bf16_pair_hw(y[4], y[5]), pack_bf16_pair_hw(y[6], y[7])};
+            } else {
+                o = u32x4v{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
+                           pack_bf16(y[6], y[7])};
+            }
+            *p = o;
+        }
     };
 
     // ---- MFMA operand reads.
@@ -217,13 +299,19 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
 #pragma unroll
     for (int st = 0; st < kStages; ++st) issue_clamped(st);
     wait_vmcnt<(kStages - 1) * CF::LOADS>();  // stage 0 landed
+    if constexpr (FUSED) {
+        transform(0, 0);
+        wait_lgkmcnt0();
+    }
     barrier();
     read_frags(0, 0, 0);
     for (int st = 0; st < nk; ++st) {
         read_frags(st & (kStages - 1), 1, 1);
         mfma(0);
         wait_vmcnt<(kStages - 2) * CF::LOADS>();  // stage st + 1 landed (st + 2, st + 3 may be in flight)
-        wait_lgkmcnt0();                           // this wave's reads of buffer st are done
+        // fused: rebuild this lane's chunks of stage st + 1 (not read by anyone yet)
+        if constexpr (FUSED) transform(st + 1, (st + 1) & (kStages - 1));
+        wait_lgkmcnt0();                           // this wave's LDS reads and writes are done
         barrier();
         issue_clamped(st + kStages);  // into buffer st, free since this barrier
         read_frags((st + 1) & (kStages - 1), 0, 0);
@@ -247,42 +335,60 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
         }
 }
 
-template <int BM, int BN, int WM, int WN>
-int launch_tiles(const ProjectArgs& a, hipStream_t stream) {
+template <int BM, int BN, int WM, int WN, bool FUSED, bool PW, int CMODE>
+int launch_tiles(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
     using CF = Cfg<BM, BN, WM, WN>;
     const int tiles_m = (int)((a.M + BM - 1) / BM);
     const int tiles_n = (int)(a.N / BN);
     const int total = a.L * tiles_m * tiles_n;
-    const size_t lds_bytes = CF::LDS_BYTES;
+    const size_t lds_bytes = CF::LDS_BYTES + ((FUSED && PW) ? (size_t)a.K * 2 : 0);
+    auto kernel = kv_project_kernel<BM, BN, WM, WN, FUSED, PW, CMODE>;
     if (lds_bytes > 65536) {
         // The opt-in above 64 KiB is per kernel and device; set it on each device once.
-        static bool attr_set[64] = {};
+        static int attr_set[64] = {};
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return -1;
         if (dev < 0 || dev >= 64) return -1;
-        if (!attr_set[dev]) {
-            if (hipFuncSetAttribute((const void*)kv_project_kernel<BM, BN, WM, WN>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) != hipSuccess)
+        if (attr_set[dev] < (int)lds_bytes) {
+            if (hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
+                hipSuccess)
                 return -1;
-            attr_set[dev] = true;
+            attr_set[dev] = (int)lds_bytes;
         }
     }
-    hipLaunchKernelGGL((kv_project_kernel<BM, BN, WM, WN>), dim3(total), dim3(CF::THREADS), lds_bytes, stream, a.A,
-                       a.B, a.C, a.M, a.K, a.N, tiles_m, tiles_n, total);
+    hipLaunchKernelGGL(kernel, dim3(total), dim3(CF::THREADS), lds_bytes, stream, a.A, a.B, a.C, a.M, a.K, a.N, a.L,
+                       tiles_m, tiles_n, total, fa);
     return 0;
+}
+
+template <bool FUSED, bool PW, int CMODE>
+int launch_shape(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
+    // 256 x 256 tiles when they fill the chip, else 128 x 128.
+    const int64_t big_tiles = (int64_t)a.L * ((a.M + 255) / 256) * (a.N / 256);
+    const int cus = a.num_cus > 0 ? a.num_cus : 256;
+    if (a.N % 256 == 0 && big_tiles >= cus) return launch_tiles<256, 256, 2, 4, FUSED, PW, CMODE>(a, fa, stream);
+    return launch_tiles<128, 128, 2, 2, FUSED, PW, CMODE>(a, fa, stream);
 }
 
 }  // namespace
 
 int launch_kv_project(const ProjectArgs& a, hipStream_t stream) {
-    // 256 x 256 tiles when they fill the chip, else 128 x 128.
-    const int64_t big_tiles = (int64_t)a.L * ((a.M + 255) / 256) * (a.N / 256);
-    const int cus = a.num_cus > 0 ? a.num_cus : 256;
+    const int rc = launch_shape<false, false, 0>(a, FusedA{nullptr, nullptr, 0.0f}, stream);
+    if (rc) return rc;
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_kv_project_fused(const ProjectArgs& a, const float* r, const uint16_t* gamma, float center,
+                            hipStream_t stream) {
+    const FusedA fa{r, gamma, center};
     int rc;
-    if (a.N % 256 == 0 && big_tiles >= cus)
-        rc = launch_tiles<256, 256, 2, 4>(a, stream);
+    if (!gamma)
+        rc = launch_shape<true, false, 0>(a, fa, stream);
+    else if (center == 0.0f)
+        rc = __builtin_signbit(center) ? launch_shape<true, true, 0>(a, fa, stream)
+                                       : launch_shape<true, true, 1>(a, fa, stream);
     else
-        rc = launch_tiles<128, 128, 2, 2>(a, stream);
+        rc = launch_shape<true, true, 2>(a, fa, stream);
     if (rc) return rc;
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -48,6 +48,8 @@ def lib():
         L.nrc_oracle_sumsq_head.restype = _f32
         L.nrc_oracle_context_norms.argtypes = [_u16p, _i64, _i64, _u16p, _u16p, _i32, _f32, _f32, _f32, _f32, _u16p]
         L.nrc_oracle_context_norms.restype = _i32
+        L.nrc_oracle_hidden_norm.argtypes = [_u16p, _i64, _i64, _u16p, _f32, _f32, _f32, _u16p, _f32p]
+        L.nrc_oracle_hidden_norm.restype = _i32
         L.nrc_oracle_kv_project.argtypes = [_u16p, _u16p, _f32p, _i32, _i64, _i64, _i64]
         L.nrc_oracle_kv_project.restype = _i32
         L.nrc_oracle_knorm_rope_head.argtypes = [_u16p, _u16p, _f32, _u16p]
@@ -137,6 +139,21 @@ def context_norms(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hidden_c
         hidden_eps, pre_eps, hidden_center, pre_center, _ptr(out, ctypes.c_uint16))
     _check(st, "context_norms")
     return out
+
+
+def hidden_norm(x, hidden_w, hidden_eps=1e-6, hidden_center=0.0, pre_eps=1e-6):
+    """x [T, 8192] bf16 bits -> (h [T, 8192] bf16 bits, r [T] float32): the
+    hidden norm's bf16 output and each row's layer-norm scale."""
+    x = _c(x, np.uint16)
+    T = x.shape[0]
+    assert x.shape == (T, D)
+    hw = None if hidden_w is None else _c(hidden_w, np.uint16)
+    h = np.empty((T, D), dtype=np.uint16)
+    r = np.empty(T, dtype=np.float32)
+    st = lib().nrc_oracle_hidden_norm(_ptr(x, ctypes.c_uint16), T, D, _ptr(hw, ctypes.c_uint16), hidden_eps,
+                                      hidden_center, pre_eps, _ptr(h, ctypes.c_uint16), _ptr(r, ctypes.c_float))
+    _check(st, "hidden_norm")
+    return h, r
 
 
 def kv_project(A, B):

@@ -198,6 +198,25 @@ int nrc_oracle_context_norms(const uint16_t *x, int64_t T, int64_t D, const uint
     return 0;
 }
 
+/* The two per-row quantities the layer norms share, as a pre-pass of a
+ * fused norms + projection computes them: h [T, 8192] bf16 (the hidden
+ * norm's output) and r [T] = rs(fma(S_p, 1/8192, pre_eps)) with S_p the row
+ * sum of squares of h. The layer outputs are bf16((h * r) * gamma_l). */
+int nrc_oracle_hidden_norm(const uint16_t *x, int64_t T, int64_t D, const uint16_t *hidden_w, float hidden_eps,
+                           float hidden_center, float pre_eps, uint16_t *h, float *r) {
+    if (D != ROW_D || T < 0 || !x || !h || !r) return ORACLE_EINVAL;
+    float *u = malloc(sizeof(float) * ROW_D);
+    if (!u) return ORACLE_EINVAL;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int c = 0; c < ROW_D; ++c) u[c] = f_of(x[t * ROW_D + c]);
+        rms_norm_row(u, hidden_w, hidden_eps, hidden_center, h + t * ROW_D);
+        for (int c = 0; c < ROW_D; ++c) u[c] = f_of(h[t * ROW_D + c]);
+        r[t] = rs(fmaf(sumsq_row(u), 0x1p-13f, pre_eps));
+    }
+    free(u);
+    return 0;
+}
+
 /* The batched projection of [RT] ContextKV._project: C[l] = A[l] B[l] with
  * A [L, T, D] bf16, B [L, D, N] bf16 (the logical operand of the bmm), C
  * [L, T, N] in FP32, each sum accumulated in FP32 in increasing d. The

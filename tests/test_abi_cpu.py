@@ -112,6 +112,22 @@ def test_store_argument_checks(lib):
     assert _store(lib, rows=0, T=0) == 0
 
 
+def test_fused_argument_checks(lib):
+    f = lib.nrc_context_hidden_norm
+    assert f(FAKE, 4, 4096, None, None, 1, 1e-6, 1e-6, 0.0, 0.0, FAKE, FAKE, None) == ENOTSUP
+    assert f(FAKE, 4, 8192, None, None, 0, 1e-6, 1e-6, 0.0, 0.0, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE, 4, 8192, None, None, 1, 1e-6, 1e-6, 0.0, 0.0, FAKE, None, None) == EINVAL
+    assert f(FAKE, 4, 8192, None, None, 1, 1e-6, 1e-6, 0.0, 0.0, MISALIGNED, FAKE, None) == EINVAL
+    assert f(None, 0, 8192, None, None, 1, 1e-6, 1e-6, 0.0, 0.0, None, None, None) == 0
+    g = lib.nrc_context_kv_project_fused
+    assert g(FAKE, FAKE, None, 0.0, FAKE, FAKE, 0, 8, 8192, 1024, None) == EINVAL
+    assert g(FAKE, FAKE, None, 0.0, FAKE, FAKE, 1, 8, 4096, 1024, None) == ENOTSUP
+    assert g(FAKE, FAKE, None, 0.0, FAKE, FAKE, 1, 8, 8192, 1000, None) == ENOTSUP
+    assert g(FAKE, None, None, 0.0, FAKE, FAKE, 1, 8, 8192, 1024, None) == EINVAL
+    assert g(FAKE, FAKE, MISALIGNED, 0.0, FAKE, FAKE, 1, 8, 8192, 1024, None) == EINVAL
+    assert g(None, None, None, 0.0, None, None, 2, 0, 8192, 1024, None) == 0
+
+
 def test_check_scalars_argument_checks(lib):
     assert lib.nrc_check_scalars(FAKE, None, None, 4, None) == EINVAL
     assert lib.nrc_check_scalars(FAKE, FAKE, None, -1, None) == EINVAL

@@ -377,8 +377,9 @@ def test_store_skips_out_of_range_rows(nrc, oracle):
 
 # --------------------------------------------------------------------- chain
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("name,T", [("tiny", 16), ("prefill", 48), ("weightless", 40)])
-def test_chain_parity(nrc, oracle, name, T):
+def test_chain_parity(nrc, oracle, name, T, fused):
     """The chain through all three calls against the oracle's chain: norms
     bit-exact, projection within tolerance, cache cells written exactly where
     the oracle writes them, with K and V within the projection's tolerance
@@ -387,17 +388,21 @@ def test_chain_parity(nrc, oracle, name, T):
 
     cfg = synth.scaled(synth.CONFIGS[name], T)
     d = synth.make_inputs(cfg, with_cache=True)
-    _say(f"chain {name} T={T}")
+    _say(f"chain {name} T={T} fused={fused}")
     caches_d = to_dev(d["caches"])
-    normed, kv = nrc.context_kv_chain(
+    L = cfg.L
+    normed = torch.empty((L, cfg.T, 8192), dtype=torch.bfloat16, device="cuda")
+    kv = nrc.context_kv_chain(
         to_dev(d["x"]), None if d["hidden_w"] is None else to_dev(d["hidden_w"]),
         None if d["pre_w"] is None else to_dev(d["pre_w"]), to_dev(d["w_kv"]), to_dev(d["positions"]),
-        to_dev(d["slots"]), None if d["cos_sin"] is None else to_dev(d["cos_sin"]), caches_d, cfg.H)
+        to_dev(d["slots"]), None if d["cos_sin"] is None else to_dev(d["cos_sin"]), caches_d, cfg.H,
+        fused=fused, workspace=None if fused else normed)
     torch.cuda.synchronize()
     want_caches = d["caches"].copy()
     o_normed, o_kv = oracle.chain(d["x"], d["hidden_w"], d["pre_w"], cfg.L, d["w_kv"], cfg.H, d["positions"],
                                   d["slots"], d["cos_sin"], want_caches, cfg.block_size)
-    assert_bits_equal(to_host(normed), o_normed, f"chain norms {name}")
+    if not fused:
+        assert_bits_equal(to_host(normed), o_normed, f"chain norms {name}")
     ok, msg = projection_tolerance_ok(to_host(kv), oracle.kv_project(o_normed, d["w_kv"]))
     assert ok, msg
     got_caches = to_host(caches_d)
@@ -420,9 +425,114 @@ def test_deterministic(nrc):
     outs = []
     for _ in range(2):
         cd = to_dev(d["caches"])
-        normed, kv = nrc.context_kv_chain(to_dev(d["x"]), to_dev(d["hidden_w"]), to_dev(d["pre_w"]),
-                                          to_dev(d["w_kv"]), to_dev(d["positions"]), to_dev(d["slots"]),
-                                          to_dev(d["cos_sin"]), cd, cfg.H)
-        outs.append((to_host(normed), to_host(kv), to_host(cd)))
+        kv = nrc.context_kv_chain(to_dev(d["x"]), to_dev(d["hidden_w"]), to_dev(d["pre_w"]), to_dev(d["w_kv"]),
+                                  to_dev(d["positions"]), to_dev(d["slots"]), to_dev(d["cos_sin"]), cd, cfg.H)
+        outs.append((to_host(kv), to_host(cd)))
     for a, b in zip(outs[0], outs[1]):
         assert np.array_equal(a, b)
+
+
+# --------------------------------------------------- fused norms + projection
+
+@pytest.mark.parametrize("name", ["tiny", "prefill", "weightless", "long", "edge"])
+def test_hidden_norm_parity_configs(nrc, oracle, name):
+    """Pre-pass of the fused path: h bit-exact and |r| bit-exact against the
+    oracle's hidden norm and layer-norm scale (edge: sampled rows incl. every
+    zero row and every finite-sum row)."""
+    cfg, d = _norms_inputs(name)
+    _say(f"hidden norm {name}: T={cfg.T}")
+    h, r = nrc.context_hidden_norm(to_dev(d["x"]), None if d["hidden_w"] is None else to_dev(d["hidden_w"]),
+                                   None if d["pre_w"] is None else to_dev(d["pre_w"]), cfg.L, d["hidden_eps"],
+                                   d["pre_eps"])
+    torch.cuda.synchronize()
+    if name == "edge":
+        xf = f32(d["x"])
+        finite_rows = np.nonzero(np.isfinite((xf.astype(np.float64) ** 2).sum(axis=1)))[0]
+        rng = np.random.default_rng(98)
+        rows = np.unique(np.concatenate([d["zero_rows"], finite_rows, rng.choice(cfg.T, 512, replace=False)]))
+    else:
+        rows = np.arange(cfg.T)
+    oh, orr = oracle.hidden_norm(np.ascontiguousarray(d["x"][rows]), d["hidden_w"], d["hidden_eps"], 0.0,
+                                 d["pre_eps"])
+    ridx = torch.from_numpy(rows).cuda()
+    assert_bits_equal(to_host(h[ridx]), oh, f"hidden norm h {name}")
+    gr = np.abs(r[ridx].cpu().numpy())
+    same = (gr.view(np.uint32) == np.abs(orr).view(np.uint32)) | (np.isnan(gr) & np.isnan(orr))
+    assert same.all(), f"hidden norm r {name}: {np.nonzero(~same)[0][:5]}"
+
+
+def _fused_vs_unfused(nrc, x, hw, pw, w_kv, L, he=1e-6, pe=1e-6, hc=0.0, pc=0.0):
+    xd, wd = to_dev(x), to_dev(w_kv)
+    hwd = None if hw is None else to_dev(hw)
+    pwd = None if pw is None else to_dev(pw)
+    normed = nrc.context_norms(xd, hwd, pwd, L, he, pe, hc, pc)
+    kv_u = nrc.context_kv_project(normed, wd)
+    h, r = nrc.context_hidden_norm(xd, hwd, pwd, L, he, pe, hc, pc)
+    kv_f = nrc.context_kv_project_fused(h, r, pwd, wd, pc)
+    torch.cuda.synchronize()
+    return to_host(kv_u), to_host(kv_f)
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill", "weightless", "long"])
+def test_fused_project_parity_configs(nrc, oracle, name):
+    """The fused projection at full size: bit-identical to the norms followed
+    by the unfused projection (both GPU; the same MFMA accumulation order),
+    and within the projection's tolerance of the oracle's FP32 sums of the
+    oracle's norms on sampled rows."""
+    cfg, d = _norms_inputs(name)
+    _say(f"fused project {name}: L={cfg.L} T={cfg.T} N={cfg.N}")
+    kv_u, kv_f = _fused_vs_unfused(nrc, d["x"], d["hidden_w"], d["pre_w"], d["w_kv"], cfg.L)
+    assert_bits_equal(kv_f, kv_u, f"fused vs unfused {name}")
+    rng = np.random.default_rng(cfg.index + 7)
+    n = min(cfg.T, 32)
+    rows = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, n, replace=False)]))
+    on = oracle.context_norms(np.ascontiguousarray(d["x"][rows]), d["hidden_w"], d["pre_w"], cfg.L)
+    ok, msg = projection_tolerance_ok(kv_f[:, rows], oracle.kv_project(on, d["w_kv"]))
+    assert ok, f"fused {name}: {msg}"
+
+
+def test_fused_project_special_values(nrc):
+    """NaN / Inf / overflow / zero rows (the exact-rounding rows of the fused
+    path), -0.0 weights, weightless layer norms and non-zero centers: fused
+    and unfused projections agree bit for bit."""
+    from norm_rope_cache_amd import synth
+
+    T, L, N = 300, 3, 256
+    x = synth.edge_mixture_bf16(91, 92, (T, 8192), nan_inf=True)
+    x[3] = 0
+    x[4] = 0x8000
+    x[5] = synth.normal_bf16(93, (8192,))
+    x[6, :] = 0x7F7F
+    x[7:40] = synth.normal_bf16(94, (33, 8192))
+    hw = synth.normal_bf16(95, (8192,), 1.0, 0.3)
+    hw[::101] = 0x8000
+    pw = synth.normal_bf16(96, (L, 8192), 1.0, 0.3)
+    pw[:, ::83] = 0x8000
+    w = synth.normal_bf16(97, (L, 8192, N), std=0.02)
+    for pre_w, hc, pc in [(pw, 0.0, 0.0), (None, 0.0, 0.0), (pw, 0.5, -0.25), (pw, -0.0, -0.0), (pw, 0.0, 0.0)]:
+        wts = pre_w
+        _say(f"fused specials pre_w={'yes' if wts is not None else 'no'} centers={hc},{pc}")
+        kv_u, kv_f = _fused_vs_unfused(nrc, x, hw, wts, w, L, 1e-6, 1e-6, hc, pc)
+        assert_bits_equal(kv_f, kv_u, f"fused vs unfused specials {hc},{pc}")
+    # a NaN layer weight forces the exact rounding on every row
+    pw_nan = pw.copy()
+    pw_nan[1, 17] = 0x7FC1
+    kv_u, kv_f = _fused_vs_unfused(nrc, x, hw, pw_nan, w, L)
+    assert_bits_equal(kv_f, kv_u, "fused vs unfused with a NaN layer weight")
+
+
+def test_fused_chain_matches_unfused_chain(nrc):
+    """context_kv_chain fused and unfused write identical caches."""
+    from norm_rope_cache_amd import synth
+
+    cfg = synth.scaled(synth.PREFILL, 200)
+    d = synth.make_inputs(cfg, with_cache=True)
+    outs = []
+    for fused in (True, False):
+        cd = to_dev(d["caches"])
+        kv = nrc.context_kv_chain(to_dev(d["x"]), to_dev(d["hidden_w"]), to_dev(d["pre_w"]), to_dev(d["w_kv"]),
+                                  to_dev(d["positions"]), to_dev(d["slots"]), to_dev(d["cos_sin"]), cd, cfg.H,
+                                  fused=fused)
+        outs.append((to_host(kv), to_host(cd)))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])

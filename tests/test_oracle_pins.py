@@ -404,6 +404,28 @@ def test_norms_layer_layout(oracle):
         assert np.array_equal(_norms(oracle, x[t:t + 1], hw, pw, L)[:, 0], out[:, t])
 
 
+def test_hidden_norm_pieces_rebuild_the_norms(oracle):
+    """The pre-pass quantities (h, r) rebuild every layer output as
+    bf16((h * r) * gamma_l): checked against the full norms on rows with
+    weights, without weights, and with a zero row."""
+    import torch
+
+    rng = np.random.default_rng(21)
+    T, L = 5, 3
+    x = bf16_bits_of(rng.standard_normal((T, D)) * 1.3)
+    x[2] = 0
+    hw = bf16_bits_of(1.0 + 0.1 * rng.standard_normal(D))
+    pw = bf16_bits_of(1.0 + 0.1 * rng.standard_normal((L, D)))
+    for w_h, w_p in ((hw, pw), (None, pw), (hw, None)):
+        full = _norms(oracle, x, w_h, w_p, L, 1e-6, 3e-3)
+        h, r = oracle.hidden_norm(x, w_h, 1e-6, 0.0, 3e-3)
+        y = f32_of_bf16(h) * r[:, None]  # float32 products, one rounding each
+        for l in range(L):
+            z = y * (f32_of_bf16(w_p[l]) if w_p is not None else np.float32(1.0))
+            want = torch.from_numpy(np.ascontiguousarray(z.astype(np.float32))).to(torch.bfloat16)
+            assert np.array_equal(full[l], want.view(torch.int16).numpy().view(np.uint16)), l
+
+
 # ------------------------------------------------------------ K-norm + RoPE
 
 def test_head_sumsq_order_golden(oracle):
