@@ -5,20 +5,25 @@
 // weight; the logical right operand is [L, D, N] with N contiguous. Results
 // are FP32 sums of exact bf16 products, rounded once to bf16.
 //
-// Kernel: one 256-thread workgroup (4 waves, 2 x 2) per BM x BN output tile
-// of one layer, K walked in steps of 64 with double-buffered LDS.
-//   - A tiles (K contiguous) go global -> registers -> LDS as 16-byte chunks.
-//   - B tiles arrive N-contiguous; each thread loads an 8(k) x NPT(n) block
-//     (one 8- or 16-byte load per k row), transposes it in registers and
-//     writes NPT rows of 8 consecutive k, so both operands sit in LDS as
-//     [row][k] with 16-byte k chunks, the layout v_mfma_f32_32x32x16_bf16
-//     reads (8 consecutive k per lane).
-//   - LDS rows are 128 bytes (64 k); chunk c of row r is stored at chunk
-//     c ^ ((r ^ (r >> 3)) & 7), which keeps both the 16-byte writes and the
-//     MFMA operand reads free of bank conflicts.
-//   - Tiles are ordered layer, M tile, N tile (N fastest); consecutive tile
-//     ids are assigned to the same XCD (workgroup ids are dealt round-robin
-//     over the 8 XCDs), so the N tiles sharing an A panel meet in one L2.
+// Kernel: one workgroup per BM x BN output tile of one layer; waves split
+// the tile WM x WN, each wave owning a (BM/WM) x (BN/WN) block of
+// v_mfma_f32_32x32x16_bf16 accumulators. K is walked in stages of 32 through
+// a 4-deep LDS ring:
+//   - both operands go global -> LDS with global_load_lds_dwordx4 (no
+//     register staging); A rows are 64 bytes per stage, B k-rows 2 BN bytes;
+//   - A fragments are read with ds_read_b128 (8 consecutive k of one row),
+//     B fragments with ds_read_b64_tr_b16, which transposes the N-contiguous
+//     B tile into the k-contiguous operand layout on the fly;
+//   - XOR swizzles on 16-byte chunks (A: chunk ^ ((row >> 2) & 3), B: chunk
+//     ^ 4 (k-row & 3)) make every fragment read cover all 64 LDS banks;
+//   - each stage is two k16 sub-steps; the loop is scheduled by hand (one
+//     LDS read or DMA between consecutive MFMAs, sched_barrier fences) so
+//     the next sub-step's fragments and the DMA of the stage four ahead are
+//     in flight while the matrix core works, with DMA issue spread over the
+//     whole stage;
+//   - consecutive tile ids go to one XCD (workgroup ids are dealt
+//     round-robin over the 8 XCDs), so tiles sharing an A panel or a B panel
+//     meet in one L2.
 #include <type_traits>
 
 #include "device_common.h"
@@ -37,6 +42,10 @@ typedef __attribute__((address_space(3))) u32x4v lds_u32x4;
 
 constexpr int kBK = 32;     // K per LDS stage
 constexpr int kStages = 4;  // LDS ring depth
+
+// 16-byte chunk swizzles of the LDS tiles (see the header).
+__device__ __forceinline__ int swz_a(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int swz_b(int krow) { return 4 * (krow & 3); }
 
 template <int BM, int BN, int WM, int WN>
 struct Cfg {
@@ -131,15 +140,15 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     // instruction written to consecutive LDS bytes). The global source of
     // each lane is chosen so that LDS holds the swizzled layouts below.
     //   A stage: row r (BM rows, 64 bytes = 4 chunks of 8 k), chunk c stored
-    //            at chunk c ^ ((r >> 1) & 3).
+    //            at chunk c ^ swz_a(r).
     //   B stage: k row r (32 rows, 2 BN bytes), 16-byte chunk c stored at
-    //            chunk c ^ (2 (r & 3)).
+    //            chunk c ^ swz_b(r).
     const uint16_t* a_src[CF::A_LOADS];
 #pragma unroll
     for (int t = 0; t < CF::A_LOADS; ++t) {
         const int off = (wave * CF::A_LOADS + t) * 1024 + lane * 16;
         const int r = off >> 6, pc = (off >> 4) & 3;
-        const int c = pc ^ ((r >> 1) & 3);
+        const int c = pc ^ swz_a(r);
         int64_t row = m0 + r;
         row = row < M ? row : M - 1;
         a_src[t] = Al + row * K + 8 * c;
@@ -149,22 +158,9 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     for (int t = 0; t < CF::B_LOADS; ++t) {
         const int off = (wave * CF::B_LOADS + t) * 1024 + lane * 16;
         const int r = off / CF::B_ROW, pc = (off % CF::B_ROW) >> 4;
-        const int c = pc ^ (2 * (r & 3));
+        const int c = pc ^ swz_b(r);
         b_src[t] = Bl + (int64_t)r * N + n0 + 8 * c;
     }
-    auto issue = [&](int s, int buf) {  // k stage s -> LDS buffer buf
-        const int64_t ka = (int64_t)s * kBK;
-        const int64_t kb = (int64_t)s * kBK * N;
-        const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-#pragma unroll
-        for (int t = 0; t < CF::A_LOADS; ++t)
-            dma16(a_src[t] + ka,
-                  __builtin_amdgcn_readfirstlane(base + buf * CF::A_BYTES + (wave * CF::A_LOADS + t) * 1024));
-#pragma unroll
-        for (int t = 0; t < CF::B_LOADS; ++t)
-            dma16(b_src[t] + kb, __builtin_amdgcn_readfirstlane(base + CF::A_REGION + buf * CF::B_BYTES +
-                                                                (wave * CF::B_LOADS + t) * 1024));
-    };
 
     // ---- fused form: the layer weights of this tile sit in LDS past the
     // ring; each lane rebuilds, in place, the A chunks its own DMA wrote:
@@ -179,7 +175,7 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
         for (int t = 0; t < CF::A_LOADS; ++t) {
             const int off = (wave * CF::A_LOADS + t) * 1024 + lane * 16;
             const int r = off >> 6, pc = (off >> 4) & 3;
-            a_kc[t] = 8 * (pc ^ ((r >> 1) & 3));
+            a_kc[t] = 8 * (pc ^ swz_a(r));
             int64_t row = m0 + r;
             row = row < M ? row : M - 1;
             const float rv = fa.r[row];
@@ -233,7 +229,7 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
         const int r = wm * CF::WTM + (lane & 31);
-        a_off[kk] = r * 64 + 16 * ((2 * kk + khalf) ^ ((r >> 1) & 3));
+        a_off[kk] = r * 64 + 16 * ((2 * kk + khalf) ^ swz_a(r));
     }
     // B (ds_read_b64_tr_b16): within each 16-lane group g, lane c = 4 jj + q
     // points at 4 bf16 of k row kbase + jj, columns 4 q .. 4 q + 3 of the
@@ -247,7 +243,7 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
 #pragma unroll
         for (int j = 0; j < CF::NI; ++j) {
             const int n = wn * CF::WTN + 32 * j + 16 * (g & 1) + 4 * q;
-            const int pc = (n >> 3) ^ (2 * jj);
+            const int pc = (n >> 3) ^ swz_b(jj);
             b_off[j] = CF::A_REGION + krow * CF::B_ROW + pc * 16 + ((n >> 2) & 1) * 8;
         }
     }
@@ -260,79 +256,136 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+    // ---- one-instruction building blocks of the scheduled loop.
+    // Fragment set f holds one k16 sub-step: af[f][i] for the wave's 32-row
+    // blocks i, bfr[f][j] for its 32-column blocks j.
     bf16x8 af[2][CF::MI], bfr[2][CF::NI];
-    auto read_frags = [&](int buf, int kk, int f) {
+    constexpr int NM = CF::MI * CF::NI;      // MFMAs per sub-step
+    constexpr int NR = CF::MI + 2 * CF::NI;  // LDS reads per sub-step
+    constexpr int HALF = CF::LOADS / 2;      // DMAs issued per sub-step
+    static_assert(CF::LOADS % 2 == 0 && HALF <= NM, "DMA spread");
+    // LDS read r of sub-step (buf, kk) into set f, in the order the MFMAs
+    // consume them: A0, B0 (two transposing halves), B1, ..., then A1, A2, ..
+    auto read_one = [&](int buf, int kk, int f, int r) {
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
         const lds_char* sa = lds + buf * CF::A_BYTES;
         const lds_char* sb = lds + buf * CF::B_BYTES;
-#pragma unroll
-        for (int i = 0; i < CF::MI; ++i)
+        if (r == 0 || r > 2 * CF::NI) {
+            const int i = r == 0 ? 0 : r - 2 * CF::NI;
             af[f][i] = *(const __attribute__((address_space(3))) bf16x8*)(sa + a_off[kk] + i * 32 * 64);
-#pragma unroll
-        for (int j = 0; j < CF::NI; ++j) {
-            const lds_char* p = sb + b_off[j] + kk * 16 * CF::B_ROW;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(p + 4 * CF::B_ROW));
-            typedef short i16x8 __attribute__((ext_vector_type(8)));
-            const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            bfr[f][j] = __builtin_bit_cast(bf16x8, both);
+        } else {
+            const int j = (r - 1) >> 1, hi = (r - 1) & 1;
+            const lds_char* p = sb + b_off[j] + kk * 16 * CF::B_ROW + hi * 4 * CF::B_ROW;
+            const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+            const i16x8 v8 = __builtin_shufflevector(v, v, 0, 1, 2, 3, 0, 1, 2, 3);
+            const i16x8 cur = __builtin_bit_cast(i16x8, bfr[f][j]);
+            const i16x8 nxt = hi ? __builtin_shufflevector(cur, v8, 0, 1, 2, 3, 8, 9, 10, 11)
+                                 : __builtin_shufflevector(v8, cur, 0, 1, 2, 3, 12, 13, 14, 15);
+            bfr[f][j] = __builtin_bit_cast(bf16x8, nxt);
         }
     };
-    auto mfma = [&](int f) {
-#pragma unroll
-        for (int i = 0; i < CF::MI; ++i)
-#pragma unroll
-            for (int j = 0; j < CF::NI; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f][i], bfr[f][j], acc[i][j], 0, 0, 0);
+    auto mfma_one = [&](int f, int idx) {
+        const int i = idx / CF::NI, j = idx % CF::NI;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f][i], bfr[f][j], acc[i][j], 0, 0, 0);
+    };
+    const int nk = (int)(K / kBK);
+    // DMA d (0 .. LOADS-1: A blocks, then B blocks) of stage st into buffer
+    // st mod 4. Past the last stage the source is clamped to stage nk - 1 and
+    // lands in a buffer nobody reads again, so every iteration issues the
+    // same number of loads and the vmcnt arithmetic is the same everywhere.
+    auto dma_one = [&](int st, int d) {
+        const int s = st < nk ? st : nk - 1;
+        const int buf = st & (kStages - 1);
+        const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+        if (d < CF::A_LOADS) {
+            dma16(a_src[d] + (int64_t)s * kBK,
+                  __builtin_amdgcn_readfirstlane(base + buf * CF::A_BYTES + (wave * CF::A_LOADS + d) * 1024));
+        } else {
+            const int t = d - CF::A_LOADS;
+            dma16(b_src[t] + (int64_t)s * kBK * N,
+                  __builtin_amdgcn_readfirstlane(base + CF::A_REGION + buf * CF::B_BYTES +
+                                                 (wave * CF::B_LOADS + t) * 1024));
+        }
     };
 
-    // ---- pipeline over stages of 32 k; DMA runs up to kStages stages ahead.
-    // Iteration s: fragments (s, 0) are in registers; read (s, 1); MFMAs of
-    // (s, 0); wait for stage s + 1's DMA and for this wave's LDS reads;
-    // barrier (stage s + 1 visible to every wave, every read of buffer s
-    // done); DMA stage s + 4 into buffer s; read (s + 1, 0); MFMAs of (s, 1).
-    const int nk = (int)(K / kBK);
-    // Every iteration issues one stage, so the vmcnt arithmetic is the same
-    // everywhere: past the last stage the source is clamped to stage nk - 1
-    // and lands in a buffer nobody reads again.
-    auto issue_clamped = [&](int st) { issue(st < nk ? st : nk - 1, st & (kStages - 1)); };
+    // ---- pipeline. Iteration st (stage st in buffer b = st mod 4, its
+    // first sub-step's fragments already in set 0):
+    //   sub-step 0: MFMAs on set 0; between them the reads of set 1 (stage
+    //               st, second sub-step) and the second half of stage
+    //               st + 3's DMA;
+    //   wait until stage st + 1 has landed (own DMAs), fused form: rebuild
+    //   this lane's A chunks of stage st + 1, then wait for this wave's LDS
+    //   traffic and barrier (stage st + 1 visible to all, buffer b free);
+    //   sub-step 1: MFMAs on set 1; between them the first half of stage
+    //               st + 4's DMA (into buffer b) and the reads of set 0 of
+    //               stage st + 1.
+    // DMA issue order is stage by stage, so "stage st + 1 landed" is
+    // vmcnt <= the loads of stages st + 2 and st + 3 = 2 LOADS.
 #pragma unroll
-    for (int st = 0; st < kStages; ++st) issue_clamped(st);
-    wait_vmcnt<(kStages - 1) * CF::LOADS>();  // stage 0 landed
+    for (int st = 0; st < kStages - 1; ++st)
+#pragma unroll
+        for (int d = 0; d < CF::LOADS; ++d) dma_one(st, d);
+#pragma unroll
+    for (int d = 0; d < HALF; ++d) dma_one(kStages - 1, d);
+    wait_vmcnt<(kStages - 2) * CF::LOADS + HALF>();  // stage 0 landed
     if constexpr (FUSED) {
         transform(0, 0);
         wait_lgkmcnt0();
     }
     barrier();
-    read_frags(0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
     for (int st = 0; st < nk; ++st) {
-        read_frags(st & (kStages - 1), 1, 1);
-        mfma(0);
-        wait_vmcnt<(kStages - 2) * CF::LOADS>();  // stage st + 1 landed (st + 2, st + 3 may be in flight)
-        // fused: rebuild this lane's chunks of stage st + 1 (not read by anyone yet)
+        const int b = st & (kStages - 1);
+#pragma unroll
+        for (int idx = 0; idx < NM; ++idx) {
+            mfma_one(0, idx);
+#pragma unroll
+            for (int r = (idx * NR) / NM; r < ((idx + 1) * NR) / NM; ++r) read_one(b, 1, 1, r);
+#pragma unroll
+            for (int d = 0; d < HALF; ++d)
+                if (idx == ((d * NM) / HALF + 1 < NM ? (d * NM) / HALF + 1 : NM - 1))
+                    dma_one(st + kStages - 1, HALF + d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_vmcnt<(kStages - 2) * CF::LOADS>();
         if constexpr (FUSED) transform(st + 1, (st + 1) & (kStages - 1));
-        wait_lgkmcnt0();                           // this wave's LDS reads and writes are done
+        wait_lgkmcnt0();
         barrier();
-        issue_clamped(st + kStages);  // into buffer st, free since this barrier
-        read_frags((st + 1) & (kStages - 1), 0, 0);
-        mfma(1);
+#pragma unroll
+        for (int idx = 0; idx < NM; ++idx) {
+            mfma_one(1, idx);
+#pragma unroll
+            for (int d = 0; d < HALF; ++d)
+                if (idx == (d * NM) / HALF) dma_one(st + kStages, d);
+#pragma unroll
+            for (int r = (idx * NR) / NM; r < ((idx + 1) * NR) / NM; ++r)
+                read_one((st + 1) & (kStages - 1), 0, 0, r);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     wait_vmcnt<0>();  // no DMA may still target this workgroup's LDS at exit
 
     // Epilogue: lane holds column (lane & 31) of each 32 x 32 block, rows
     // 8 (v / 4) + 4 (lane / 32) + (v % 4).
     uint16_t* Cl = C + (int64_t)layer * M * N;
+    auto store_tile = [&](auto checked) {
 #pragma unroll
-    for (int i = 0; i < CF::MI; ++i)
+        for (int i = 0; i < CF::MI; ++i)
 #pragma unroll
-        for (int j = 0; j < CF::NI; ++j) {
-            const int64_t col = n0 + wn * CF::WTN + 32 * j + (lane & 31);
+            for (int j = 0; j < CF::NI; ++j) {
+                const int64_t col = n0 + wn * CF::WTN + 32 * j + (lane & 31);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = m0 + wm * CF::WTM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (row < M) Cl[row * N + col] = (uint16_t)to_bf16(acc[i][j][v]);
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t row = m0 + wm * CF::WTM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    if (!decltype(checked)::value || row < M) Cl[row * N + col] = (uint16_t)to_bf16(acc[i][j][v]);
+                }
             }
-        }
+    };
+    if (m0 + BM <= M)
+        store_tile(std::false_type{});
+    else
+        store_tile(std::true_type{});
 }
 
 template <int BM, int BN, int WM, int WN, bool FUSED, bool PW, int CMODE>
