@@ -164,23 +164,25 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
 
     // ---- fused form: the layer weights of this tile sit in LDS past the
     // ring; each lane rebuilds, in place, the A chunks its own DMA wrote:
-    // a = bf16((h * r) * gamma) per element (paired hardware conversion on
-    // rows flagged NaN-free, the exact rounding otherwise).
+    // a = bf16((h * |r|) * gamma) per element with the paired hardware
+    // conversion (round to nearest even; a NaN stays a NaN, and any NaN
+    // operand makes the FP32 sum NaN, which the epilogue writes as 0x7FC0,
+    // so the C tile matches the one computed from the exactly rounded
+    // norms). All of a lane's chunks sit at the same k chunk, so one weight
+    // read serves them all. The work is split into pieces (reads, one
+    // element pair, a write) that the loop places between MFMAs.
     constexpr int G_OFF = CF::LDS_BYTES;
     float a_r[CF::A_LOADS];
-    bool a_slow[CF::A_LOADS];
-    int a_kc[CF::A_LOADS];
+    int a_kc = 0;
     if constexpr (FUSED) {
 #pragma unroll
         for (int t = 0; t < CF::A_LOADS; ++t) {
             const int off = (wave * CF::A_LOADS + t) * 1024 + lane * 16;
             const int r = off >> 6, pc = (off >> 4) & 3;
-            a_kc[t] = 8 * (pc ^ swz_a(r));
+            a_kc = 8 * (pc ^ swz_a(r));  // the same for every t
             int64_t row = m0 + r;
             row = row < M ? row : M - 1;
-            const float rv = fa.r[row];
-            a_slow[t] = __builtin_signbit(rv);
-            a_r[t] = __builtin_fabsf(rv);
+            a_r[t] = __builtin_fabsf(fa.r[row]);
         }
         if constexpr (PW) {
             const uint16_t* g = fa.gamma + (int64_t)layer * K;
@@ -192,32 +194,35 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
         }
         __syncthreads();  // the weights are visible before the first transform
     }
-    auto transform = [&](int st, int buf) {
+    u32x4v t_h[CF::A_LOADS], t_g;
+    uint32_t t_o[CF::A_LOADS][4];
+    auto t_chunk = [&](int buf, int t) {
+        return (lds_u32x4*)(lds + buf * CF::A_BYTES + (wave * CF::A_LOADS + t) * 1024 + lane * 16);
+    };
+    auto t_read = [&](int st, int buf) {
         const int sk = st < (int)(K / kBK) ? st : (int)(K / kBK) - 1;
 #pragma unroll
+        for (int t = 0; t < CF::A_LOADS; ++t) t_h[t] = *t_chunk(buf, t);
+        if constexpr (PW) t_g = *(const lds_u32x4*)(lds + G_OFF + 2 * (sk * kBK + a_kc));
+    };
+    auto t_pair = [&](int t, int q) {
+        float y0 = bf16_lo(t_h[t][q]) * a_r[t];
+        float y1 = bf16_hi(t_h[t][q]) * a_r[t];
+        if constexpr (PW) {
+            const float g0 = bf16_lo(t_g[q]), g1 = bf16_hi(t_g[q]);
+            y0 = y0 * (CMODE == 2 ? g0 + fa.center : g0);
+            y1 = y1 * (CMODE == 2 ? g1 + fa.center : g1);
+        }
+        t_o[t][q] = pack_bf16_pair_hw(y0, y1);
+    };
+    auto t_write = [&](int buf, int t) { *t_chunk(buf, t) = u32x4v{t_o[t][0], t_o[t][1], t_o[t][2], t_o[t][3]}; };
+    auto transform = [&](int st, int buf) {
+        t_read(st, buf);
+#pragma unroll
         for (int t = 0; t < CF::A_LOADS; ++t) {
-            lds_u32x4* p = (lds_u32x4*)(lds + buf * CF::A_BYTES + (wave * CF::A_LOADS + t) * 1024 + lane * 16);
-            const u32x4v hv = *p;
-            float y[8] = {bf16_lo(hv.x), bf16_hi(hv.x), bf16_lo(hv.y), bf16_hi(hv.y),
-                          bf16_lo(hv.z), bf16_hi(hv.z), bf16_lo(hv.w), bf16_hi(hv.w)};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = y[e] * a_r[t];
-            if constexpr (PW) {
-                const u32x4v gv = *(const lds_u32x4*)(lds + G_OFF + 2 * (sk * kBK + a_kc[t]));
-                float g[8] = {bf16_lo(gv.x), bf16_hi(gv.x), bf16_lo(gv.y), bf16_hi(gv.y),
-                              bf16_lo(gv.z), bf16_hi(gv.z), bf16_lo(gv.w), bf16_hi(gv.w)};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] = y[e] * (CMODE == 2 ? g[e] + fa.center : g[e]);
-            }
-            u32x4v o;
-            if (!a_slow[t]) {
-                o = u32x4v{pack_bf16_pair_hw(y[0], y[1]), pack_bf16_pair_hw(y[2], y[3]),
-                           pack_bf16_pair_hw(y[4], y[5]), pack_bf16_pair_hw(y[6], y[7])};
-            } else {
-                o = u32x4v{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
-                           pack_bf16(y[6], y[7])};
-            }
-            *p = o;
+            for (int q = 0; q < 4; ++q) t_pair(t, q);
+            t_write(buf, t);
         }
     };
 
@@ -313,9 +318,10 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     //   sub-step 0: MFMAs on set 0; between them the reads of set 1 (stage
     //               st, second sub-step) and the second half of stage
     //               st + 3's DMA;
-    //   wait until stage st + 1 has landed (own DMAs), fused form: rebuild
-    //   this lane's A chunks of stage st + 1, then wait for this wave's LDS
-    //   traffic and barrier (stage st + 1 visible to all, buffer b free);
+    //   wait until stage st + 1 has landed (own DMAs; the fused form waits
+    //   at the top instead and rebuilds its A chunks during sub-step 0),
+    //   then wait for this wave's LDS traffic and barrier (stage st + 1
+    //   visible to all, buffer b free);
     //   sub-step 1: MFMAs on set 1; between them the first half of stage
     //               st + 4's DMA (into buffer b) and the reads of set 0 of
     //               stage st + 1.
@@ -335,11 +341,29 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     barrier();
 #pragma unroll
     for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
+    // Fused form: the A chunks of stage st + 1 are rebuilt during sub-step
+    // 0, so that stage is waited for at the top of the iteration (vmcnt <=
+    // stage st + 2 and the first half of st + 3); its reads go in the first
+    // slot, its element pairs over the remaining slots, each chunk written
+    // back after its last pair.
+    constexpr int NP = 4 * CF::A_LOADS;  // element pairs per lane per stage
+    auto pair_slot = [](int p) { return NM > 1 ? 1 + (p * (NM - 1)) / NP : 0; };
     for (int st = 0; st < nk; ++st) {
         const int b = st & (kStages - 1);
+        const int b1 = (st + 1) & (kStages - 1);
+        if constexpr (FUSED) wait_vmcnt<CF::LOADS + HALF>();
 #pragma unroll
         for (int idx = 0; idx < NM; ++idx) {
             mfma_one(0, idx);
+            if constexpr (FUSED) {
+                if (idx == 0) t_read(st + 1, b1);
+#pragma unroll
+                for (int p = 0; p < NP; ++p)
+                    if (pair_slot(p) == idx) {
+                        t_pair(p >> 2, p & 3);
+                        if ((p & 3) == 3) t_write(b1, p >> 2);
+                    }
+            }
 #pragma unroll
             for (int r = (idx * NR) / NM; r < ((idx + 1) * NR) / NM; ++r) read_one(b, 1, 1, r);
 #pragma unroll
@@ -348,8 +372,7 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
                     dma_one(st + kStages - 1, HALF + d);
             __builtin_amdgcn_sched_barrier(0);
         }
-        wait_vmcnt<(kStages - 2) * CF::LOADS>();
-        if constexpr (FUSED) transform(st + 1, (st + 1) & (kStages - 1));
+        if constexpr (!FUSED) wait_vmcnt<(kStages - 2) * CF::LOADS>();
         wait_lgkmcnt0();
         barrier();
 #pragma unroll
@@ -359,8 +382,7 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
             for (int d = 0; d < HALF; ++d)
                 if (idx == (d * NM) / HALF) dma_one(st + kStages, d);
 #pragma unroll
-            for (int r = (idx * NR) / NM; r < ((idx + 1) * NR) / NM; ++r)
-                read_one((st + 1) & (kStages - 1), 0, 0, r);
+            for (int r = (idx * NR) / NM; r < ((idx + 1) * NR) / NM; ++r) read_one(b1, 0, 0, r);
             __builtin_amdgcn_sched_barrier(0);
         }
     }

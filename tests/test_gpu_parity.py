@@ -71,6 +71,10 @@ def test_scalars_exhaustive(nrc, oracle):
         assert_bits_equal(gb, ob, f"bf16 chunk {start:#x}")
         nan = np.isnan(x)
         assert_bits_equal(np.where(nan, 0, pair), np.where(nan, 0, ob), f"paired bf16 chunk {start:#x} (non-NaN)")
+        # the fused projection feeds these conversions to the matrix cores,
+        # where any NaN operand gives a NaN sum: every NaN must stay a NaN
+        pn = pair[nan]
+        assert (((pn & 0x7F80) == 0x7F80) & ((pn & 0x7F) != 0)).all(), f"paired bf16 chunk {start:#x}: NaN lost"
         same = (gr.view(np.uint32) == orr.view(np.uint32)) | (np.isnan(gr) & np.isnan(orr))
         if not same.all():
             i = int(np.nonzero(~same)[0][0])
