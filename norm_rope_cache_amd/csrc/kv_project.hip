@@ -112,24 +112,36 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
     lds_char* lds = (lds_char*)lds_raw;
 
-    // XCD-aware tile id: workgroup b runs on XCD b % 8; give each XCD a
-    // contiguous range of tiles (N fastest), so the N tiles that share an
-    // A panel run side by side under one L2.
-    int tile = blockIdx.x;
-    if ((total_tiles & 7) == 0) tile = (blockIdx.x & 7) * (total_tiles >> 3) + (blockIdx.x >> 3);
-    const int tn = tile % tiles_n;
-    int tm, layer;
-    if constexpr (FUSED) {
-        layer = (tile / tiles_n) % L;
-        tm = tile / (tiles_n * L);
-    } else {
-        tm = (tile / tiles_n) % tiles_m;
-        layer = tile / (tiles_n * tiles_m);
-    }
-    const int64_t m0 = (int64_t)tm * BM;
-    const int64_t n0 = (int64_t)tn * BN;
-    const uint16_t* Al = FUSED ? A : A + (int64_t)layer * M * K;
-    const uint16_t* Bl = B + (int64_t)layer * K * N;
+    // Persistent workgroups: workgroup b takes the tiles tile_of(0),
+    // tile_of(1), ... Workgroup b runs on XCD b % 8; when both the tile
+    // count and the grid split evenly over the 8 XCDs, each XCD owns a
+    // contiguous range of tile ids (N fastest), so tiles sharing an A panel
+    // or a B panel run side by side under one L2.
+    const int G = (int)gridDim.x;
+    const bool xcd_split = (total_tiles & 7) == 0 && (G & 7) == 0;
+    auto tile_of = [&](int it) -> int {
+        if (xcd_split) {
+            const int loc = (int)(blockIdx.x >> 3) + it * (G >> 3);
+            return loc < (total_tiles >> 3) ? (int)(blockIdx.x & 7) * (total_tiles >> 3) + loc : total_tiles;
+        }
+        const int t = (int)blockIdx.x + it * G;
+        return t < total_tiles ? t : total_tiles;
+    };
+    int layer = 0;
+    int64_t m0 = 0, n0 = 0;
+    auto decode = [&](int tile) {
+        const int tn = tile % tiles_n;
+        int tm;
+        if constexpr (FUSED) {
+            layer = (tile / tiles_n) % L;
+            tm = tile / (tiles_n * L);
+        } else {
+            tm = (tile / tiles_n) % tiles_m;
+            layer = tile / (tiles_n * tiles_m);
+        }
+        m0 = (int64_t)tm * BM;
+        n0 = (int64_t)tn * BN;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -144,23 +156,27 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     //   B stage: k row r (32 rows, 2 BN bytes), 16-byte chunk c stored at
     //            chunk c ^ swz_b(r).
     const uint16_t* a_src[CF::A_LOADS];
-#pragma unroll
-    for (int t = 0; t < CF::A_LOADS; ++t) {
-        const int off = (wave * CF::A_LOADS + t) * 1024 + lane * 16;
-        const int r = off >> 6, pc = (off >> 4) & 3;
-        const int c = pc ^ swz_a(r);
-        int64_t row = m0 + r;
-        row = row < M ? row : M - 1;
-        a_src[t] = Al + row * K + 8 * c;
-    }
     const uint16_t* b_src[CF::B_LOADS];
+    auto set_sources = [&]() {
+        const uint16_t* Al = FUSED ? A : A + (int64_t)layer * M * K;
+        const uint16_t* Bl = B + (int64_t)layer * K * N;
 #pragma unroll
-    for (int t = 0; t < CF::B_LOADS; ++t) {
-        const int off = (wave * CF::B_LOADS + t) * 1024 + lane * 16;
-        const int r = off / CF::B_ROW, pc = (off % CF::B_ROW) >> 4;
-        const int c = pc ^ swz_b(r);
-        b_src[t] = Bl + (int64_t)r * N + n0 + 8 * c;
-    }
+        for (int t = 0; t < CF::A_LOADS; ++t) {
+            const int off = (wave * CF::A_LOADS + t) * 1024 + lane * 16;
+            const int r = off >> 6, pc = (off >> 4) & 3;
+            const int c = pc ^ swz_a(r);
+            int64_t row = m0 + r;
+            row = row < M ? row : M - 1;
+            a_src[t] = Al + row * K + 8 * c;
+        }
+#pragma unroll
+        for (int t = 0; t < CF::B_LOADS; ++t) {
+            const int off = (wave * CF::B_LOADS + t) * 1024 + lane * 16;
+            const int r = off / CF::B_ROW, pc = (off % CF::B_ROW) >> 4;
+            const int c = pc ^ swz_b(r);
+            b_src[t] = Bl + (int64_t)r * N + n0 + 8 * c;
+        }
+    };
 
     // ---- fused form: the layer weights of this tile sit in LDS past the
     // ring; each lane rebuilds, in place, the A chunks its own DMA wrote:
@@ -173,27 +189,33 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     // element pair, a write) that the loop places between MFMAs.
     constexpr int G_OFF = CF::LDS_BYTES;
     float a_r[CF::A_LOADS];
-    int a_kc = 0;
-    if constexpr (FUSED) {
+    const int a_kc = 8 * ((lane & 3) ^ swz_a(lane >> 2));  // k chunk of every A chunk this lane owns
+    int staged_layer = -1;
+    // Per-tile fused state: each owned row's scale, and (when the layer
+    // changes) the layer weight staged in LDS. Called only when no wave
+    // still reads the weights of the previous tile.
+    auto set_fused = [&]() {
+        if constexpr (FUSED) {
 #pragma unroll
-        for (int t = 0; t < CF::A_LOADS; ++t) {
-            const int off = (wave * CF::A_LOADS + t) * 1024 + lane * 16;
-            const int r = off >> 6, pc = (off >> 4) & 3;
-            a_kc = 8 * (pc ^ swz_a(r));  // the same for every t
-            int64_t row = m0 + r;
-            row = row < M ? row : M - 1;
-            a_r[t] = __builtin_fabsf(fa.r[row]);
-        }
-        if constexpr (PW) {
-            const uint16_t* g = fa.gamma + (int64_t)layer * K;
-            for (int c = tid; c < (int)(K / 8); c += CF::THREADS) {
-                U32x4 w = load16(g + 8 * c);
-                if constexpr (CMODE == 1) w = plus_zero16(w);
-                *(lds_u32x4*)(lds + G_OFF + 16 * c) = u32x4v{w.x, w.y, w.z, w.w};
+            for (int t = 0; t < CF::A_LOADS; ++t) {
+                const int off = (wave * CF::A_LOADS + t) * 1024 + lane * 16;
+                int64_t row = m0 + (off >> 6);
+                row = row < M ? row : M - 1;
+                a_r[t] = __builtin_fabsf(fa.r[row]);
+            }
+            if constexpr (PW) {
+                if (layer != staged_layer) {
+                    const uint16_t* g = fa.gamma + (int64_t)layer * K;
+                    for (int c = tid; c < (int)(K / 8); c += CF::THREADS) {
+                        U32x4 w = load16(g + 8 * c);
+                        if constexpr (CMODE == 1) w = plus_zero16(w);
+                        *(lds_u32x4*)(lds + G_OFF + 16 * c) = u32x4v{w.x, w.y, w.z, w.w};
+                    }
+                    staged_layer = layer;
+                }
             }
         }
-        __syncthreads();  // the weights are visible before the first transform
-    }
+    };
     u32x4v t_h[CF::A_LOADS], t_g;
     uint32_t t_o[CF::A_LOADS][4];
     auto t_chunk = [&](int buf, int t) {
@@ -254,12 +276,6 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     }
 
     f32x16 acc[CF::MI][CF::NI];
-#pragma unroll
-    for (int i = 0; i < CF::MI; ++i)
-#pragma unroll
-        for (int j = 0; j < CF::NI; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     // ---- one-instruction building blocks of the scheduled loop.
     // Fragment set f holds one k16 sub-step: af[f][i] for the wave's 32-row
@@ -327,87 +343,131 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     //               stage st + 1.
     // DMA issue order is stage by stage, so "stage st + 1 landed" is
     // vmcnt <= the loads of stages st + 2 and st + 3 = 2 LOADS.
+    // ---- tiles. The first tile's setup and prologue DMA (stages 0-2 and
+    // the first half of stage 3) go out before the loop; each later tile's
+    // go out as soon as the previous tile's K loop has finished, before that
+    // tile's results are stored, so the store burst and the first loads of
+    // the next tile overlap.
+    auto issue_prologue = [&]() {
 #pragma unroll
-    for (int st = 0; st < kStages - 1; ++st)
+        for (int st = 0; st < kStages - 1; ++st)
 #pragma unroll
-        for (int d = 0; d < CF::LOADS; ++d) dma_one(st, d);
+            for (int d = 0; d < CF::LOADS; ++d) dma_one(st, d);
 #pragma unroll
-    for (int d = 0; d < HALF; ++d) dma_one(kStages - 1, d);
-    wait_vmcnt<(kStages - 2) * CF::LOADS + HALF>();  // stage 0 landed
-    if constexpr (FUSED) {
-        transform(0, 0);
-        wait_lgkmcnt0();
-    }
-    barrier();
-#pragma unroll
-    for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
-    // Fused form: the A chunks of stage st + 1 are rebuilt during sub-step
-    // 0, so that stage is waited for at the top of the iteration (vmcnt <=
-    // stage st + 2 and the first half of st + 3); its reads go in the first
-    // slot, its element pairs over the remaining slots, each chunk written
-    // back after its last pair.
-    constexpr int NP = 4 * CF::A_LOADS;  // element pairs per lane per stage
-    auto pair_slot = [](int p) { return NM > 1 ? 1 + (p * (NM - 1)) / NP : 0; };
-    for (int st = 0; st < nk; ++st) {
-        const int b = st & (kStages - 1);
-        const int b1 = (st + 1) & (kStages - 1);
-        if constexpr (FUSED) wait_vmcnt<CF::LOADS + HALF>();
-#pragma unroll
-        for (int idx = 0; idx < NM; ++idx) {
-            mfma_one(0, idx);
-            if constexpr (FUSED) {
-                if (idx == 0) t_read(st + 1, b1);
-#pragma unroll
-                for (int p = 0; p < NP; ++p)
-                    if (pair_slot(p) == idx) {
-                        t_pair(p >> 2, p & 3);
-                        if ((p & 3) == 3) t_write(b1, p >> 2);
-                    }
-            }
-#pragma unroll
-            for (int r = (idx * NR) / NM; r < ((idx + 1) * NR) / NM; ++r) read_one(b, 1, 1, r);
-#pragma unroll
-            for (int d = 0; d < HALF; ++d)
-                if (idx == ((d * NM) / HALF + 1 < NM ? (d * NM) / HALF + 1 : NM - 1))
-                    dma_one(st + kStages - 1, HALF + d);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if constexpr (!FUSED) wait_vmcnt<(kStages - 2) * CF::LOADS>();
-        wait_lgkmcnt0();
-        barrier();
-#pragma unroll
-        for (int idx = 0; idx < NM; ++idx) {
-            mfma_one(1, idx);
-#pragma unroll
-            for (int d = 0; d < HALF; ++d)
-                if (idx == (d * NM) / HALF) dma_one(st + kStages, d);
-#pragma unroll
-            for (int r = (idx * NR) / NM; r < ((idx + 1) * NR) / NM; ++r) read_one(b1, 0, 0, r);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    wait_vmcnt<0>();  // no DMA may still target this workgroup's LDS at exit
-
+        for (int d = 0; d < HALF; ++d) dma_one(kStages - 1, d);
+    };
+    int it = 0;
+    int tile = tile_of(0);
+    if (tile >= total_tiles) return;
+    decode(tile);
+    set_sources();
+    set_fused();
+    issue_prologue();
     // Epilogue: lane holds column (lane & 31) of each 32 x 32 block, rows
     // 8 (v / 4) + 4 (lane / 32) + (v % 4).
-    uint16_t* Cl = C + (int64_t)layer * M * N;
+    auto epilogue = [&](int e_layer, int64_t e_m0, int64_t e_n0) {
+    uint16_t* Cl = C + (int64_t)e_layer * M * N;
     auto store_tile = [&](auto checked) {
 #pragma unroll
         for (int i = 0; i < CF::MI; ++i)
 #pragma unroll
             for (int j = 0; j < CF::NI; ++j) {
-                const int64_t col = n0 + wn * CF::WTN + 32 * j + (lane & 31);
+                const int64_t col = e_n0 + wn * CF::WTN + 32 * j + (lane & 31);
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int64_t row = m0 + wm * CF::WTM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    const int64_t row = e_m0 + wm * CF::WTM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                     if (!decltype(checked)::value || row < M) Cl[row * N + col] = (uint16_t)to_bf16(acc[i][j][v]);
                 }
             }
     };
-    if (m0 + BM <= M)
+    if (e_m0 + BM <= M)
         store_tile(std::false_type{});
     else
         store_tile(std::true_type{});
+    };
+
+    while (true) {
+#pragma unroll
+        for (int i = 0; i < CF::MI; ++i)
+#pragma unroll
+            for (int j = 0; j < CF::NI; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+        // Stage 0 landed. On the first tile: vmcnt <= stages 1-2 and half of
+        // 3; later tiles also have the previous tile's stores in flight,
+        // issued after these loads, so wait for everything.
+        if (it == 0)
+            wait_vmcnt<(kStages - 2) * CF::LOADS + HALF>();
+        else
+            wait_vmcnt<0>();
+        if constexpr (FUSED) __syncthreads();  // staged weights visible to every wave
+        if constexpr (FUSED) {
+            transform(0, 0);
+            wait_lgkmcnt0();
+        }
+        barrier();
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
+        // Fused form: the A chunks of stage st + 1 are rebuilt during sub-step
+        // 0, so that stage is waited for at the top of the iteration (vmcnt <=
+        // stage st + 2 and the first half of st + 3); its reads go in the first
+        // slot, its element pairs over the remaining slots, each chunk written
+        // back after its last pair.
+        constexpr int NP = 4 * CF::A_LOADS;  // element pairs per lane per stage
+        auto pair_slot = [](int p) { return NM > 1 ? 1 + (p * (NM - 1)) / NP : 0; };
+        for (int st = 0; st < nk; ++st) {
+            const int b = st & (kStages - 1);
+            const int b1 = (st + 1) & (kStages - 1);
+            if constexpr (FUSED) wait_vmcnt<CF::LOADS + HALF>();
+#pragma unroll
+            for (int idx = 0; idx < NM; ++idx) {
+                mfma_one(0, idx);
+                if constexpr (FUSED) {
+                    if (idx == 0) t_read(st + 1, b1);
+#pragma unroll
+                    for (int p = 0; p < NP; ++p)
+                        if (pair_slot(p) == idx) {
+                            t_pair(p >> 2, p & 3);
+                            if ((p & 3) == 3) t_write(b1, p >> 2);
+                        }
+                }
+#pragma unroll
+                for (int r = (idx * NR) / NM; r < ((idx + 1) * NR) / NM; ++r) read_one(b, 1, 1, r);
+#pragma unroll
+                for (int d = 0; d < HALF; ++d)
+                    if (idx == ((d * NM) / HALF + 1 < NM ? (d * NM) / HALF + 1 : NM - 1))
+                        dma_one(st + kStages - 1, HALF + d);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (!FUSED) wait_vmcnt<(kStages - 2) * CF::LOADS>();
+            wait_lgkmcnt0();
+            barrier();
+#pragma unroll
+            for (int idx = 0; idx < NM; ++idx) {
+                mfma_one(1, idx);
+#pragma unroll
+                for (int d = 0; d < HALF; ++d)
+                    if (idx == (d * NM) / HALF) dma_one(st + kStages, d);
+#pragma unroll
+                for (int r = (idx * NR) / NM; r < ((idx + 1) * NR) / NM; ++r) read_one(b1, 0, 0, r);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        wait_vmcnt<0>();  // the clamped loads past the last stage have landed
+        barrier();         // every wave is done with the ring and the weights
+        const int e_layer = layer;
+        const int64_t e_m0 = m0, e_n0 = n0;
+        const int next = tile_of(++it);
+        if (next < total_tiles) {
+            decode(next);
+            set_sources();
+            set_fused();
+            issue_prologue();
+        }
+        epilogue(e_layer, e_m0, e_n0);
+        if (next >= total_tiles) break;
+    }
+    wait_vmcnt<0>();  // no DMA may still target this workgroup's LDS at exit
 }
 
 template <int BM, int BN, int WM, int WN, bool FUSED, bool PW, int CMODE>
@@ -431,7 +491,12 @@ int launch_tiles(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
             attr_set[dev] = (int)lds_bytes;
         }
     }
-    hipLaunchKernelGGL(kernel, dim3(total), dim3(CF::THREADS), lds_bytes, stream, a.A, a.B, a.C, a.M, a.K, a.N, a.L,
+    // One persistent workgroup per LDS-resident slot (the ring and weights
+    // take most of a CU's 160 KiB), never more than there are tiles.
+    const int per_cu = (int)(163840 / lds_bytes) < 1 ? 1 : (int)(163840 / lds_bytes);
+    const int cus = a.num_cus > 0 ? a.num_cus : 256;
+    const int grid = total < per_cu * cus ? total : per_cu * cus;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(CF::THREADS), lds_bytes, stream, a.A, a.B, a.C, a.M, a.K, a.N, a.L,
                        tiles_m, tiles_n, total, fa);
     return 0;
 }

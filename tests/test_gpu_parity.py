@@ -210,6 +210,22 @@ def test_project_shapes(nrc, oracle, T, N):
     _project_check(nrc, oracle, A, B, rows, f"project T={T} N={N}")
 
 
+@pytest.mark.parametrize("L,T,N", [(4, 3000, 1024), (2, 4196, 2048), (1, 8292, 2560)])
+def test_project_several_tiles_per_workgroup(nrc, oracle, L, T, N):
+    """Shapes with more output tiles than resident workgroups, so each
+    workgroup walks several tiles: 768 tiles of 128 x 128 (ragged last row
+    tile), 272 tiles of 256 x 256 (split evenly over the XCDs) and 330 of
+    256 x 256 (not a multiple of 8: round-robin assignment). Sampled rows,
+    the ragged tail included, against the oracle's FP32 sums."""
+    from norm_rope_cache_amd import synth
+
+    A = synth.normal_bf16(5000 + T, (L, T, 8192))
+    B = synth.normal_bf16(6000 + N, (L, 8192, N), std=0.02)
+    rows = np.unique(np.concatenate([[0, T - 1], np.arange(1, T, max(1, T // 48)), np.arange(T - 60, T)]))
+    _say(f"project multi-tile L={L} T={T} N={N}")
+    _project_check(nrc, oracle, A, B, rows, f"project multi-tile L={L} T={T} N={N}")
+
+
 def test_project_one_hot_and_zero_rows(nrc, oracle):
     """A one-hot row selects a row of B: the result is that row's bf16 value
     exactly; an all-zero row gives +0."""
@@ -493,6 +509,23 @@ def test_fused_project_parity_configs(nrc, oracle, name):
     on = oracle.context_norms(np.ascontiguousarray(d["x"][rows]), d["hidden_w"], d["pre_w"], cfg.L)
     ok, msg = projection_tolerance_ok(kv_f[:, rows], oracle.kv_project(on, d["w_kv"]))
     assert ok, f"fused {name}: {msg}"
+
+
+def test_fused_project_layer_changes_within_a_workgroup(nrc):
+    """276 tiles of 256 x 256 over three layers (not a multiple of 8, so
+    tiles go round-robin): the workgroups that take a second tile take it
+    from another layer and restage its weight. Fused equals unfused bit for
+    bit."""
+    from norm_rope_cache_amd import synth
+
+    L, T, N = 3, 5633, 1024
+    x = synth.normal_bf16(7001, (T, 8192))
+    hw = synth.normal_bf16(7002, (8192,), 1.0, 0.3)
+    pw = synth.normal_bf16(7003, (L, 8192), 1.0, 0.3)
+    w = synth.normal_bf16(7004, (L, 8192, N), std=0.02)
+    _say(f"fused multi-tile L={L} T={T} N={N}")
+    kv_u, kv_f = _fused_vs_unfused(nrc, x, hw, pw, w, L)
+    assert_bits_equal(kv_f, kv_u, "fused vs unfused, several tiles per workgroup")
 
 
 def test_fused_project_special_values(nrc):
