@@ -97,7 +97,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=1536)
     ap.add_argument("--path", choices=("fused", "unfused"), default="unfused")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device-to-device once, a known-size reference for HBM byte counters")

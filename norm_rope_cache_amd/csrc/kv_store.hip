@@ -105,8 +105,11 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restric
         page = s32 - block * block_size;
     }
     uint16_t* dst = layers.cache[l] + ((((int64_t)block * H + h) * block_size + page) * (2 * kHeadDim)) + 8 * g;
-    store16(dst, out);
-    store16(dst + kHeadDim, vw);
+    // Non-temporal: the cache rows are scattered and not read back by this
+    // chain, so they go out to HBM now instead of lingering dirty in the
+    // caches until the next kernel's traffic evicts them.
+    store16_nt(dst, out);
+    store16_nt(dst + kHeadDim, vw);
 }
 
 int launch_kv_store(const KvStoreArgs& a, hipStream_t stream) {
