@@ -97,6 +97,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true", help="skip timing the norm variants after the chain")
     ap.add_argument("--cpu-rows", type=int, default=1536)
     ap.add_argument("--path", choices=("fused", "unfused"), default="unfused")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -224,6 +225,30 @@ def main():
 
     rows_per_s = cfg.T * args.steps / wall
 
+    # Norm variants (FP32 weights, weights scaling the norms' inputs), timed
+    # after the chain on the same rows: not part of the step.
+    variants = {}
+    if not args.no_variants and hw is not None and pw is not None:
+        hw32, pw32 = hw.float().contiguous(), pw.float().contiguous()
+        vout = torch.empty((cfg.L, cfg.T, 8192), dtype=torch.bfloat16, device=dev)
+        vb = cfg.T * (2 * 8192 + 2 * cfg.L * 8192) + 4 * 8192 * (1 + cfg.L)
+        for his, pis in ((False, False), (True, True)):
+            run = lambda: nrc.context_norms_ex(x, hw32, pw32, cfg.L, d["hidden_eps"], d["pre_eps"],
+                                               hidden_input_scale=his, pre_input_scale=pis, out=vout)
+            for _ in range(3):
+                run()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            name = "context_norms_ex[fp32 weights" + (", input-scaled]" if his else "]")
+            variants[name] = {"bound": "hbm", "ms": ms, "bytes": vb, "achieved_GBs": vb / (ms * 1e-3) / 1e9,
+                              "frac": vb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log("variants: " + ", ".join(f"{k}={v['ms']:.4f} ms" for k, v in variants.items()))
+
     cpu = None
     if not args.no_cpu_baseline:
         rows = min(args.cpu_rows, cfg.T)
@@ -259,6 +284,7 @@ def main():
         },
         "roofline": roofline,
         "kernels": kernels,
+        "variants": variants,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -67,6 +67,39 @@ int32_t nrc_context_norms(const uint16_t* x, int64_t T, int64_t D, const uint16_
                           const uint16_t* pre_w, int32_t L, float hidden_eps, float pre_eps,
                           float hidden_center, float pre_center, uint16_t* out, void* stream);
 
+/* Weight kinds and flags of nrc_context_norms_ex. */
+#define NRC_WEIGHT_NONE 0
+#define NRC_WEIGHT_BF16 1
+#define NRC_WEIGHT_F32 2
+#define NRC_HIDDEN_INPUT_SCALE 1u
+#define NRC_PRE_INPUT_SCALE 2u
+
+/*
+ * nrc_context_norms_ex - nrc_context_norms with every weight form the norms
+ * accept. Page "...cutedsl.draft.context", ContextNorms and
+ * ContextNormConstants (each norm's weight absent, BF16 or FP32; whether the
+ * weight scales the norm's input instead of its output); arithmetic of both
+ * forms per "...draft_boundary", boundary_fragments.
+ *
+ *   hidden_w, hidden_kind  NRC_WEIGHT_NONE with NULL, NRC_WEIGHT_BF16 with
+ *              [D] bf16, or NRC_WEIGHT_F32 with [D] float; 16-byte aligned.
+ *   pre_w, pre_kind        the same for [L, D] layer weights.
+ *   flags      NRC_HIDDEN_INPUT_SCALE / NRC_PRE_INPUT_SCALE: that norm's
+ *              weight scales its input. Ignored for a weightless norm.
+ *   Other arguments as nrc_context_norms.
+ * gamma = w + center (FP32 add). Output-scaled: r = 1/sqrt(S(x)/D + eps),
+ * y = (x * r) * gamma. Input-scaled: v = gamma * x, r = 1/sqrt(S(v)/D +
+ * eps), y = v * r (input-scaled layer norms: one sum per layer). S in the
+ * library's fixed order; y rounded to bf16 (nearest even, NaN -> 0x7FC0).
+ * With no FP32 weight and no flag the result is nrc_context_norms'.
+ * T == 0 returns NRC_OK. Errors: NRC_EINVAL (kind out of range, a pointer
+ * NULL or not NULL against its kind, unknown flags, NULL x or out with
+ * T > 0, T < 0, L < 1, misalignment), NRC_ENOTSUP (D != 8192).
+ */
+int32_t nrc_context_norms_ex(const uint16_t* x, int64_t T, int64_t D, const void* hidden_w, int32_t hidden_kind,
+                             const void* pre_w, int32_t pre_kind, int32_t L, float hidden_eps, float pre_eps,
+                             float hidden_center, float pre_center, uint32_t flags, uint16_t* out, void* stream);
+
 /*
  * nrc_context_kv_project - the batched K/V projection C[l] = A[l] . B[l].
  * Page "...runtime.draft", ContextKV._project (the bmm of the stacked layer

@@ -70,6 +70,9 @@ def _load():
     L.nrc_abi_version.argtypes = []
     L.nrc_context_norms.restype = _i32
     L.nrc_context_norms.argtypes = [_vp, _i64, _i64, _vp, _vp, _i32, _f32, _f32, _f32, _f32, _vp, _vp]
+    L.nrc_context_norms_ex.restype = _i32
+    L.nrc_context_norms_ex.argtypes = [_vp, _i64, _i64, _vp, _i32, _vp, _i32, _i32, _f32, _f32, _f32, _f32,
+                                       ctypes.c_uint32, _vp, _vp]
     L.nrc_context_kv_project.restype = _i32
     L.nrc_context_kv_project.argtypes = [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp]
     L.nrc_context_kv_store.restype = _i32
@@ -148,6 +151,50 @@ def context_norms(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hidden_c
             raise ValueError("out must be [L, T, D]")
     _check(_load().nrc_context_norms(_ptr(x), T, D, _ptr(hidden_w), _ptr(pre_w), L, hidden_eps, pre_eps,
                                      hidden_center, pre_center, _ptr(out), _stream(stream)))
+    return out
+
+
+WEIGHT_NONE, WEIGHT_BF16, WEIGHT_F32 = 0, 1, 2
+HIDDEN_INPUT_SCALE, PRE_INPUT_SCALE = 1, 2
+
+
+def _weight_kind(w, name, shape):
+    import torch
+
+    if w is None:
+        return WEIGHT_NONE
+    if not w.is_cuda or not w.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if tuple(w.shape) != shape:
+        raise ValueError(f"{name} must be {list(shape)}")
+    if w.dtype == torch.bfloat16:
+        return WEIGHT_BF16
+    if w.dtype == torch.float32:
+        return WEIGHT_F32
+    raise ValueError(f"{name} must be bf16 or float32, not {w.dtype}")
+
+
+def context_norms_ex(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hidden_center=0.0, pre_center=0.0,
+                     hidden_input_scale=False, pre_input_scale=False, out=None, stream=None):
+    """context_norms with bf16 or float32 weights and, per norm, the weight
+    scaling the norm's input instead of its output."""
+    import torch
+
+    _bf16(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [T, 8192]")
+    T, D = x.shape
+    hk = _weight_kind(hidden_w, "hidden_w", (D,))
+    pk = _weight_kind(pre_w, "pre_w", (L, D))
+    if out is None:
+        out = torch.empty((L, T, D), dtype=torch.bfloat16, device=x.device)
+    else:
+        _bf16(out, "out")
+        if tuple(out.shape) != (L, T, D):
+            raise ValueError("out must be [L, T, D]")
+    flags = (HIDDEN_INPUT_SCALE if hidden_input_scale else 0) | (PRE_INPUT_SCALE if pre_input_scale else 0)
+    _check(_load().nrc_context_norms_ex(_ptr(x), T, D, _ptr(hidden_w), hk, _ptr(pre_w), pk, L, hidden_eps, pre_eps,
+                                        hidden_center, pre_center, flags, _ptr(out), _stream(stream)))
     return out
 
 

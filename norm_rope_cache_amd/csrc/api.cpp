@@ -75,6 +75,39 @@ int32_t nrc_context_norms(const uint16_t* x, int64_t T, int64_t D, const uint16_
     return launch_status(nrc::launch_context_norms(a, (hipStream_t)stream), "context_norms");
 }
 
+int32_t nrc_context_norms_ex(const uint16_t* x, int64_t T, int64_t D, const void* hidden_w, int32_t hidden_kind,
+                             const void* pre_w, int32_t pre_kind, int32_t L, float hidden_eps, float pre_eps,
+                             float hidden_center, float pre_center, uint32_t flags, uint16_t* out, void* stream) {
+    if (D != NRC_HIDDEN) return fail(NRC_ENOTSUP, "context_norms_ex: rows of %lld, not %d", (long long)D, NRC_HIDDEN);
+    if (T < 0) return fail(NRC_EINVAL, "context_norms_ex: T = %lld < 0", (long long)T);
+    if (L < 1) return fail(NRC_EINVAL, "context_norms_ex: L = %d < 1", L);
+    if (hidden_kind < NRC_WEIGHT_NONE || hidden_kind > NRC_WEIGHT_F32 || pre_kind < NRC_WEIGHT_NONE ||
+        pre_kind > NRC_WEIGHT_F32)
+        return fail(NRC_EINVAL, "context_norms_ex: weight kinds %d, %d (0 none, 1 bf16, 2 FP32)", hidden_kind,
+                    pre_kind);
+    if ((hidden_kind == NRC_WEIGHT_NONE) != (hidden_w == nullptr) || (pre_kind == NRC_WEIGHT_NONE) != (pre_w == nullptr))
+        return fail(NRC_EINVAL, "context_norms_ex: a weight pointer must be NULL exactly when its kind is none");
+    if (flags & ~(uint32_t)(NRC_HIDDEN_INPUT_SCALE | NRC_PRE_INPUT_SCALE))
+        return fail(NRC_EINVAL, "context_norms_ex: unknown flags 0x%x", flags);
+    if (T > ((int64_t)1 << 40) / ((int64_t)L * D))
+        return fail(NRC_EINVAL, "context_norms_ex: output of %lld x %d rows too large", (long long)T, L);
+    if (T == 0) return NRC_OK;
+    if (!x || !out) return fail(NRC_EINVAL, "context_norms_ex: NULL x or out");
+    if (!aligned(x, 16) || !aligned(out, 16) || (hidden_w && !aligned(hidden_w, 16)) ||
+        (pre_w && !aligned(pre_w, 16)))
+        return fail(NRC_EINVAL, "context_norms_ex: operands must be 16-byte aligned");
+    const bool plain = hidden_kind != NRC_WEIGHT_F32 && pre_kind != NRC_WEIGHT_F32 && flags == 0;
+    if (plain) {
+        nrc::NormsArgs a{x, T, (const uint16_t*)hidden_w, (const uint16_t*)pre_w, L, hidden_eps, pre_eps,
+                         hidden_center, pre_center, out, num_cus()};
+        return launch_status(nrc::launch_context_norms(a, (hipStream_t)stream), "context_norms_ex");
+    }
+    nrc::NormsExArgs a{x, T, hidden_w, hidden_kind, pre_w, pre_kind, L, hidden_eps, pre_eps, hidden_center,
+                       pre_center, (flags & NRC_HIDDEN_INPUT_SCALE) != 0, (flags & NRC_PRE_INPUT_SCALE) != 0, out,
+                       num_cus()};
+    return launch_status(nrc::launch_norms_ex(a, (hipStream_t)stream), "context_norms_ex");
+}
+
 int32_t nrc_context_hidden_norm(const uint16_t* x, int64_t T, int64_t D, const uint16_t* hidden_w,
                                 const uint16_t* pre_w, int32_t L, float hidden_eps, float pre_eps,
                                 float hidden_center, float pre_center, uint16_t* h, float* r, void* stream) {

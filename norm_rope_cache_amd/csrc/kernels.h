@@ -45,6 +45,23 @@ struct NormsArgs {
     int32_t num_cus;
 };
 
+// The norms with FP32 weights and/or input-scaled weights (norms_ex.hip).
+struct NormsExArgs {
+    const uint16_t* x;
+    int64_t T;
+    const void* hidden_w;  // kind 0: nullptr; 1: bf16 [8192]; 2: float [8192]
+    int32_t hidden_kind;
+    const void* pre_w;     // [L, 8192] of pre_kind's type, or nullptr
+    int32_t pre_kind;
+    int32_t L;
+    float hidden_eps, pre_eps, hidden_center, pre_center;
+    bool hidden_input_scale, pre_input_scale;
+    uint16_t* out;
+    int num_cus;
+};
+
+int launch_norms_ex(const NormsExArgs& a, hipStream_t stream);
+
 int launch_context_norms(const NormsArgs& a, hipStream_t stream);
 // h_out [T, 8192] bf16 and r_out [T]: the pre-pass of the fused projection (a.out unused).
 int launch_hidden_norm(const NormsArgs& a, uint16_t* h_out, float* r_out, hipStream_t stream);

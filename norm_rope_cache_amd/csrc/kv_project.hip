@@ -435,7 +435,7 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
                 for (int r = (idx * NR) / NM; r < ((idx + 1) * NR) / NM; ++r) read_one(b, 1, 1, r);
 #pragma unroll
                 for (int d = 0; d < HALF; ++d)
-                    if (idx == ((d * NM) / HALF + 1 < NM ? (d * NM) / HALF + 1 : NM - 1))
+                    if (idx == ((d * NM) / HALF + 2 < NM ? (d * NM) / HALF + 2 : NM - 1))
                         dma_one(st + kStages - 1, HALF + d);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -447,7 +447,7 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
                 mfma_one(1, idx);
 #pragma unroll
                 for (int d = 0; d < HALF; ++d)
-                    if (idx == (d * NM) / HALF) dma_one(st + kStages, d);
+                    if (idx == ((d * NM) / HALF + 1 < NM ? (d * NM) / HALF + 1 : NM - 1)) dma_one(st + kStages, d);
 #pragma unroll
                 for (int r = (idx * NR) / NM; r < ((idx + 1) * NR) / NM; ++r) read_one(b1, 0, 0, r);
                 __builtin_amdgcn_sched_barrier(0);

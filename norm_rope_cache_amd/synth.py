@@ -115,6 +115,12 @@ def normal_bf16(seed, shape, mean=0.0, std=1.0):
     return out.reshape(shape)
 
 
+def normal_f32(seed, shape, mean=0.0, std=1.0):
+    """float32 values of mean + std * N(0, 1) (FP32 norm weights)."""
+    n = int(np.prod(shape))
+    return (mean + std * normal(seed, n)).astype(np.float32).reshape(shape)
+
+
 def random_bits_u16(seed, shape):
     """Uniform random 16-bit patterns (e.g. a cache's prior contents)."""
     n = int(np.prod(shape))

@@ -48,6 +48,9 @@ def lib():
         L.nrc_oracle_sumsq_head.restype = _f32
         L.nrc_oracle_context_norms.argtypes = [_u16p, _i64, _i64, _u16p, _u16p, _i32, _f32, _f32, _f32, _f32, _u16p]
         L.nrc_oracle_context_norms.restype = _i32
+        L.nrc_oracle_context_norms_ex.restype = _i32
+        L.nrc_oracle_context_norms_ex.argtypes = [_u16p, _i64, _i64, ctypes.c_void_p, _i32, ctypes.c_void_p, _i32, _i32,
+                                                  _f32, _f32, _f32, _f32, _i32, _u16p]
         L.nrc_oracle_hidden_norm.argtypes = [_u16p, _i64, _i64, _u16p, _f32, _f32, _f32, _u16p, _f32p]
         L.nrc_oracle_hidden_norm.restype = _i32
         L.nrc_oracle_kv_project.argtypes = [_u16p, _u16p, _f32p, _i32, _i64, _i64, _i64]
@@ -138,6 +141,43 @@ def context_norms(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hidden_c
         _ptr(x, ctypes.c_uint16), T, D, _ptr(hw, ctypes.c_uint16), _ptr(pw, ctypes.c_uint16), L,
         hidden_eps, pre_eps, hidden_center, pre_center, _ptr(out, ctypes.c_uint16))
     _check(st, "context_norms")
+    return out
+
+
+def _weight(w, shape):
+    """(kind, contiguous array) of a norm weight: None, bf16 bits (uint16) or
+    FP32 values (float32)."""
+    if w is None:
+        return 0, None
+    w = np.asarray(w)
+    if w.dtype == np.uint16:
+        kind = 1
+    elif w.dtype == np.float32:
+        kind = 2
+    else:
+        raise TypeError(f"norm weight of dtype {w.dtype}: expected uint16 (bf16 bits) or float32")
+    w = np.ascontiguousarray(w)
+    assert w.shape == shape, (w.shape, shape)
+    return kind, w
+
+
+def context_norms_ex(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hidden_center=0.0, pre_center=0.0,
+                     hidden_input_scale=False, pre_input_scale=False):
+    """The norms with bf16 or FP32 weights (uint16 bits or float32 arrays,
+    None for weightless) and, per norm, the weight scaling the input instead
+    of the output. x [T, 8192] bf16 bits -> [L, T, 8192] bf16 bits."""
+    x = _c(x, np.uint16)
+    T = x.shape[0]
+    assert x.shape == (T, D)
+    hk, hw = _weight(hidden_w, (D,))
+    pk, pw = _weight(pre_w, (L, D))
+    out = np.empty((L, T, D), dtype=np.uint16)
+    flags = (1 if hidden_input_scale else 0) | (2 if pre_input_scale else 0)
+    st = lib().nrc_oracle_context_norms_ex(
+        _ptr(x, ctypes.c_uint16), T, D, None if hw is None else hw.ctypes.data, hk,
+        None if pw is None else pw.ctypes.data, pk, L, hidden_eps, pre_eps, hidden_center, pre_center, flags,
+        _ptr(out, ctypes.c_uint16))
+    _check(st, "context_norms_ex")
     return out
 
 

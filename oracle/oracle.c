@@ -108,16 +108,44 @@ static float sumsq_row(const float *u) {
     return fold(group, ROW_LANES / ROW_WAVE);
 }
 
-/* One RMSNorm of a row as the boundary page's row-norm arithmetic states it:
- * r = rs(fma(S, 1/D, eps)), y = x * r, then y * gamma (gamma = w + center) when
- * the norm has a weight; out = bf16(y). 1/8192 = 2^-13 is exact. */
-static void rms_norm_row(const float *u, const uint16_t *w, float eps, float center, uint16_t *out) {
-    float r = rs(fmaf(sumsq_row(u), 0x1p-13f, eps));
+/* A norm's weight: none, bf16 bits or FP32 values ([CTX] ContextNormConstants:
+ * a weight is absent, BF16 or FP32). gamma[c] = w[c] + center, one FP32 add
+ * ([CTX] _ContextNormsKernel adds the gain center to every loaded weight). */
+enum { W_NONE = 0, W_BF16 = 1, W_F32 = 2 };
+typedef struct {
+    int kind;
+    const void *w;
+    float center;
+} weight_t;
+
+static float gamma_of(const weight_t *g, int c) {
+    float w = g->kind == W_BF16 ? f_of(((const uint16_t *)g->w)[c]) : ((const float *)g->w)[c];
+    return w + g->center;
+}
+
+/* One RMSNorm of a row as the boundary page's row-norm arithmetic states it
+ * ([BND] boundary_fragments): r = rs(fma(S, 1/D, eps)). Output-scaled (the
+ * default): S sums the squares of x, y = x * r, then y * gamma. Input-scaled
+ * (the weight scales the input): v = gamma * x first, S sums the squares of
+ * v, y = v * r and no weight afterwards. out = bf16(y). 1/8192 = 2^-13. */
+static void rms_norm_row_ex(const float *u, const weight_t *g, int input_scale, float eps, uint16_t *out) {
+    float *v = malloc(sizeof(float) * ROW_D);
+    if (!v) abort();
+    const int scale_in = g->kind != W_NONE && input_scale;
+    for (int c = 0; c < ROW_D; ++c) v[c] = scale_in ? gamma_of(g, c) * u[c] : u[c];
+    float r = rs(fmaf(sumsq_row(v), 0x1p-13f, eps));
     for (int c = 0; c < ROW_D; ++c) {
-        float y = u[c] * r;
-        if (w) y = y * (f_of(w[c]) + center);
+        float y = v[c] * r;
+        if (g->kind != W_NONE && !scale_in) y = y * gamma_of(g, c);
         out[c] = bf(y);
     }
+    free(v);
+}
+
+/* The default form: bf16 weight (or none) applied to the norm's output. */
+static void rms_norm_row(const float *u, const uint16_t *w, float eps, float center, uint16_t *out) {
+    weight_t g = {w ? W_BF16 : W_NONE, w, center};
+    rms_norm_row_ex(u, &g, 0, eps, out);
 }
 
 /* ----------------------------------------------------- 64-wide head K-norm */
@@ -192,6 +220,42 @@ int nrc_oracle_context_norms(const uint16_t *x, int64_t T, int64_t D, const uint
         for (int32_t l = 0; l < L; ++l)
             rms_norm_row(u, pre_w ? pre_w + (int64_t)l * ROW_D : NULL, pre_eps, pre_center,
                          out + ((int64_t)l * T + t) * ROW_D);
+    }
+    free(u);
+    free(h);
+    return 0;
+}
+
+/* The norms with every variant the context page's norms accept ([CTX]
+ * ContextNorms, ContextNormConstants): each weight absent, bf16 or FP32
+ * (hidden_kind / pre_kind: 0, 1, 2; pre_w is [L, 8192] of that type), gain
+ * centers, and per norm whether the weight scales its input (flags bit 0:
+ * hidden, bit 1: the layer norms) instead of its output. With the layer
+ * norms input-scaled, each layer has its own sum of squares. */
+int nrc_oracle_context_norms_ex(const uint16_t *x, int64_t T, int64_t D, const void *hidden_w, int32_t hidden_kind,
+                                const void *pre_w, int32_t pre_kind, int32_t L, float hidden_eps, float pre_eps,
+                                float hidden_center, float pre_center, int32_t flags, uint16_t *out) {
+    if (D != ROW_D || T < 0 || L < 1 || !x || !out) return ORACLE_EINVAL;
+    if (hidden_kind < W_NONE || hidden_kind > W_F32 || pre_kind < W_NONE || pre_kind > W_F32) return ORACLE_EINVAL;
+    if ((hidden_kind == W_NONE) != (hidden_w == NULL) || (pre_kind == W_NONE) != (pre_w == NULL)) return ORACLE_EINVAL;
+    float *u = malloc(sizeof(float) * ROW_D);
+    uint16_t *h = malloc(sizeof(uint16_t) * ROW_D);
+    if (!u || !h) {
+        free(u);
+        free(h);
+        return ORACLE_EINVAL;
+    }
+    const weight_t gh = {hidden_kind, hidden_w, hidden_center};
+    const size_t pre_elem = pre_kind == W_F32 ? sizeof(float) : sizeof(uint16_t);
+    for (int64_t t = 0; t < T; ++t) {
+        for (int c = 0; c < ROW_D; ++c) u[c] = f_of(x[t * ROW_D + c]);
+        rms_norm_row_ex(u, &gh, flags & 1, hidden_eps, h);
+        for (int c = 0; c < ROW_D; ++c) u[c] = f_of(h[c]);
+        for (int32_t l = 0; l < L; ++l) {
+            const weight_t gl = {pre_kind, pre_w ? (const char *)pre_w + (size_t)l * ROW_D * pre_elem : NULL,
+                                 pre_center};
+            rms_norm_row_ex(u, &gl, (flags >> 1) & 1, pre_eps, out + ((int64_t)l * T + t) * ROW_D);
+        }
     }
     free(u);
     free(h);

@@ -66,6 +66,30 @@ def test_norms_argument_checks(lib):
     assert f(None, 0, 8192, None, None, 3, 1e-6, 1e-6, 0.0, 0.0, None, None) == 0
 
 
+def test_norms_ex_argument_checks(lib):
+    f = lib.nrc_context_norms_ex
+    ok = dict(x=FAKE, T=4, D=8192, hw=None, hk=0, pw=None, pk=0, L=1, flags=0, out=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["T"], a["D"], a["hw"], a["hk"], a["pw"], a["pk"], a["L"], 1e-6, 1e-6, 0.0, 0.0,
+                 a["flags"], a["out"], None)
+
+    assert call(D=4096) == ENOTSUP
+    assert call(T=-1) == EINVAL
+    assert call(L=0) == EINVAL
+    assert call(hk=3, hw=FAKE) == EINVAL
+    assert call(pk=-1) == EINVAL
+    assert call(hk=1) == EINVAL            # bf16 kind without a pointer
+    assert call(hw=FAKE) == EINVAL         # pointer with kind none
+    assert call(pk=2) == EINVAL
+    assert call(flags=4) == EINVAL
+    assert call(x=None) == EINVAL
+    assert call(out=MISALIGNED) == EINVAL
+    assert call(hk=2, hw=MISALIGNED) == EINVAL
+    assert call(T=0, x=None, out=None) == 0
+
+
 def test_project_argument_checks(lib):
     f = lib.nrc_context_kv_project
     assert f(FAKE, FAKE, FAKE, 0, 8, 8192, 1024, None) == EINVAL

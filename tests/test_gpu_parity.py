@@ -165,6 +165,77 @@ def test_norms_special_values(nrc, oracle):
         assert_bits_equal(to_host(out), want, f"norms specials {he},{pe},{hc},{pc}")
 
 
+# ------------------------------------------ norm variants (FP32, input scale)
+
+def _variant_weights(kind, shape, seed):
+    from norm_rope_cache_amd import synth
+
+    if kind is None:
+        return None
+    if kind == "bf16":
+        return synth.normal_bf16(seed, shape, 1.0, 0.4)
+    return synth.normal_f32(seed, shape, 1.0, 0.4)
+
+
+@pytest.mark.parametrize("hk", [None, "bf16", "f32"])
+@pytest.mark.parametrize("pk", [None, "bf16", "f32"])
+def test_norms_ex_parity(nrc, oracle, hk, pk):
+    """Every weight kind of each norm, output- and input-scaled, with and
+    without gain centers: bit-exact against the oracle on ragged T."""
+    from norm_rope_cache_amd import synth
+
+    T, L = 37, 3
+    x = synth.normal_bf16(9001, (T, 8192), 0.0, 1.5)
+    x[3] = 0
+    hw = _variant_weights(hk, (8192,), 9002)
+    pw = _variant_weights(pk, (L, 8192), 9003)
+    for his in (False, True):
+        for pis in (False, True):
+            for hc, pc in ((0.0, 0.0), (0.25, -0.5)):
+                _say(f"norms_ex hk={hk} pk={pk} in={his},{pis} centers={hc},{pc}")
+                got = nrc.context_norms_ex(to_dev(x), None if hw is None else to_dev(hw),
+                                           None if pw is None else to_dev(pw), L, 1e-6, 2e-6, hc, pc, his, pis)
+                want = oracle.context_norms_ex(x, hw, pw, L, 1e-6, 2e-6, hc, pc, his, pis)
+                assert_bits_equal(to_host(got), want, f"norms_ex {hk} {pk} {his} {pis} {hc} {pc}")
+
+
+def test_norms_ex_special_values_and_grid_stride(nrc, oracle):
+    """NaN / Inf / subnormal / near-max rows, -0 and zero FP32 weights, eps = 0,
+    and more rows than workgroups (grid stride), both norms input-scaled."""
+    from norm_rope_cache_amd import synth
+
+    T, L = 2300, 2
+    x = synth.normal_bf16(9101, (T, 8192))
+    x[:64] = synth.edge_mixture_bf16(9102, 9103, (64, 8192), nan_inf=True)
+    x[64] = 0x8000
+    x[65, :] = 0x7F7F
+    hw = synth.normal_f32(9104, (8192,), 1.0, 0.5)
+    hw[::101] = -0.0
+    hw[7] = 0.0
+    pw = synth.normal_f32(9105, (L, 8192), 1.0, 0.5)
+    pw[1, ::89] = -0.0
+    for he, pe, his, pis in ((1e-6, 1e-6, True, True), (0.0, 0.0, True, False), (0.0, 1e-6, False, True)):
+        _say(f"norms_ex specials eps={he},{pe} in={his},{pis}")
+        got = to_host(nrc.context_norms_ex(to_dev(x), to_dev(hw), to_dev(pw), L, he, pe, 0.0, 0.0, his, pis))
+        rows = np.unique(np.concatenate([np.arange(70), np.arange(70, T, 37), [T - 1]]))
+        want = oracle.context_norms_ex(np.ascontiguousarray(x[rows]), hw, pw, L, he, pe, 0.0, 0.0, his, pis)
+        assert_bits_equal(got[:, rows], want, f"norms_ex specials {he},{pe},{his},{pis}")
+
+
+def test_norms_ex_plain_form_is_the_norms(nrc):
+    """bf16 weights on the outputs through the general entry: the same bits as
+    context_norms (it takes the same kernel)."""
+    from norm_rope_cache_amd import synth
+
+    T, L = 300, 4
+    x = to_dev(synth.normal_bf16(9201, (T, 8192)))
+    hw = to_dev(synth.normal_bf16(9202, (8192,), 1.0, 0.3))
+    pw = to_dev(synth.normal_bf16(9203, (L, 8192), 1.0, 0.3))
+    a = to_host(nrc.context_norms(x, hw, pw, L, 1e-6, 1e-6, 0.5, 0.0))
+    b = to_host(nrc.context_norms_ex(x, hw, pw, L, 1e-6, 1e-6, 0.5, 0.0))
+    assert_bits_equal(b, a, "norms_ex plain form")
+
+
 # ---------------------------------------------------------------- projection
 
 def _project_check(nrc, oracle, A, B, rows=None, what=""):

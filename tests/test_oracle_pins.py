@@ -426,6 +426,123 @@ def test_hidden_norm_pieces_rebuild_the_norms(oracle):
             assert np.array_equal(full[l], want.view(torch.int16).numpy().view(np.uint16)), l
 
 
+# ------------------------------------------- norm variants (FP32, input scale)
+
+def _bf16_round_indep(f):
+    """bf16 bits of float32 values (no NaN) by the midpoint rule in float64,
+    independently of the oracle's bit trick."""
+    f = np.asarray(f, dtype=np.float32)
+    bits = f.view(np.uint32)
+    lo = (bits >> 16).astype(np.uint16)
+    hi = (lo + 1).astype(np.uint16)
+    vlo = f32_of_bf16(lo).astype(np.float64)
+    vhi = f32_of_bf16(hi).astype(np.float64)
+    x = f.astype(np.float64)
+    dlo, dhi = np.abs(x - vlo), np.abs(vhi - x)
+    return np.where((dhi < dlo) | ((dhi == dlo) & ((lo & 1) == 1)), hi, lo).astype(np.uint16)
+
+
+def test_norms_ex_default_form_equals_the_norms(oracle):
+    """The general entry with bf16 weights applied to the outputs is the plain
+    norms; FP32 weights holding exactly the bf16 values give the same bits."""
+    rng = np.random.default_rng(31)
+    T, L = 4, 3
+    x = bf16_bits_of(rng.standard_normal((T, D)))
+    hw = bf16_bits_of(1.0 + 0.2 * rng.standard_normal(D))
+    pw = bf16_bits_of(1.0 + 0.2 * rng.standard_normal((L, D)))
+    want = oracle.context_norms(x, hw, pw, L, 1e-6, 1e-6, 0.25, -0.5)
+    got = oracle.context_norms_ex(x, hw, pw, L, 1e-6, 1e-6, 0.25, -0.5)
+    assert np.array_equal(got, want)
+    got32 = oracle.context_norms_ex(x, f32_of_bf16(hw), f32_of_bf16(pw), L, 1e-6, 1e-6, 0.25, -0.5)
+    assert np.array_equal(got32, want)
+
+
+def test_norms_input_scaled_constant_rows_are_unit(oracle):
+    """Page '...draft_boundary', boundary_fragments, input-scaled form:
+    v = gamma x, S sums v^2, y = v r, no weight afterwards. A constant row
+    x = +-2^k with a constant gamma c (8 significant bits) has S = 8192 (c x)^2
+    exactly, so y = v / |v| rounds to exactly +-1: the hidden output is +-1
+    whatever c is (the output-scaled form would give +-c), and each input-
+    scaled layer norm of it, with its own constant c_l, again gives +-1 (each
+    layer has its own sum). Negative c flips the sign."""
+    ks = [-12, 0, 3, 20]
+    rows = []
+    for k in ks:
+        rows.append(np.full(D, 2.0 ** k))
+        rows.append(np.full(D, -(2.0 ** k)))
+    x = bf16_bits_of(np.stack(rows))
+    sign = np.signbit(f32_of_bf16(x))
+    L = 3
+    for c, cl in ((1.5, [0.75, 3.0, 5.0]), (-2.5, [1.25, -0.375, 40.0])):
+        for kind in ("bf16", "f32"):
+            hw = np.full(D, c, dtype=np.float32)
+            pw = np.stack([np.full(D, v, dtype=np.float32) for v in cl])
+            if kind == "bf16":
+                hw, pw = bf16_bits_of(hw), bf16_bits_of(pw)
+            out = oracle.context_norms_ex(x, hw, pw, L, 0.0, 0.0, 0.0, 0.0, True, True)
+            h_neg = sign ^ (c < 0)
+            for l in range(L):
+                neg = h_neg ^ (cl[l] < 0)
+                assert np.array_equal(out[l], np.where(neg, np.uint16(0xBF80), np.uint16(0x3F80))), (c, kind, l)
+            # hidden input-scaled, layers output-scaled: +-c_l exactly
+            out = oracle.context_norms_ex(x, hw, pw, L, 0.0, 0.0, 0.0, 0.0, True, False)
+            for l in range(L):
+                mag = bf16_bits_of(np.full(D, abs(cl[l]), dtype=np.float32))
+                neg = h_neg ^ (cl[l] < 0)
+                assert np.array_equal(out[l], np.where(neg, mag | np.uint16(0x8000), mag)), (c, kind, l)
+
+
+def test_norms_ex_large_eps_closed_form(oracle):
+    """With eps = 2^20 and rows of |x| <= 0.25, fma(S, 2^-13, eps) = 2^20
+    exactly (S 2^-13 is below half an ulp of 2^20), so r = 2^-10 exactly and
+    each norm reduces to one rounded product: output-scaled
+    bf16((x 2^-10) gamma), input-scaled bf16((gamma x) 2^-10), gamma =
+    w + center. The expected bits come from numpy's IEEE float32 products and
+    a midpoint-rule bf16 rounding. Random FP32 weights carry bits below bf16
+    precision, so reading them through bf16 would change many outputs."""
+    rng = np.random.default_rng(41)
+    T, L = 3, 2
+    x = bf16_bits_of(np.clip(rng.standard_normal((T, D)) * 0.08, -0.25, 0.25))
+    eps = np.float32(2.0 ** 20)
+    r = np.float32(2.0 ** -10)
+    hc, pc = np.float32(0.125), np.float32(-0.0625)
+    for hk in ("bf16", "f32", None):
+        for pk in ("bf16", "f32", None):
+            hw = (1.0 + 0.3 * rng.standard_normal(D)).astype(np.float32)
+            pw = (1.0 + 0.3 * rng.standard_normal((L, D))).astype(np.float32)
+            if hk == "bf16":
+                hw = bf16_bits_of(hw)
+            if pk == "bf16":
+                pw = bf16_bits_of(pw)
+            hwv = None if hk is None else (f32_of_bf16(hw) if hk == "bf16" else hw)
+            pwv = None if pk is None else (f32_of_bf16(pw) if pk == "bf16" else pw)
+            for his in (False, True):
+                for pis in (False, True):
+                    got = oracle.context_norms_ex(x, None if hk is None else hw, None if pk is None else pw, L,
+                                                  float(eps), float(eps), float(hc), float(pc), his, pis)
+                    xf = f32_of_bf16(x)
+                    if hwv is None:
+                        hy = xf * r
+                    elif his:
+                        hy = ((hwv + hc) * xf) * r
+                    else:
+                        hy = (xf * r) * (hwv + hc)
+                    hf = f32_of_bf16(_bf16_round_indep(hy))
+                    for l in range(L):
+                        if pwv is None:
+                            y = hf * r
+                        elif pis:
+                            y = ((pwv[l] + pc) * hf) * r
+                        else:
+                            y = (hf * r) * (pwv[l] + pc)
+                        assert np.array_equal(got[l], _bf16_round_indep(y)), (hk, pk, his, pis, l)
+    if True:  # the FP32 weights do matter: their bf16 copies give other bits
+        hw = (1.0 + 0.3 * rng.standard_normal(D)).astype(np.float32)
+        a = oracle.context_norms_ex(x, hw, None, 1, float(eps), float(eps))
+        b = oracle.context_norms_ex(x, bf16_bits_of(hw), None, 1, float(eps), float(eps))
+        assert (a != b).mean() > 0.05
+
+
 # ------------------------------------------------------------ K-norm + RoPE
 
 def test_head_sumsq_order_golden(oracle):
