@@ -199,6 +199,39 @@ int32_t nrc_context_kv_store(const uint16_t* k, const uint16_t* v, int64_t k_lay
                              int32_t H, int32_t L, float eps, void* stream);
 
 /*
+ * nrc_context_kv_store_ex - nrc_context_kv_store with the pages' full
+ * operand surface: page "...cutedsl.draft.context", ContextKvStore (strided
+ * key-cache views: block, page and head strides, K then V in a 128-element
+ * run), and page "...runtime.draft", _slot_groups (a per-layer slot list,
+ * None for a layer that stores nothing, runs of layers with lists of their
+ * own length).
+ *
+ *   slots    host array of L pointers: layer l's int64 slot list, 8-byte
+ *            aligned, or NULL (the layer stores nothing; caches[l] unused).
+ *   rows     host array of L counts: the first rows[l] rows of layer l are
+ *            inserted, 0 <= rows[l] <= T (ignored where slots[l] is NULL).
+ *   caches   host array of L pointers at K of (block 0, page 0, head 0) of
+ *            each layer's cache, 16-byte aligned. (block, page, head) lives
+ *            at block * block_stride + page * page_stride + head *
+ *            head_stride elements: K in [0, 64), V in [64, 128). Strides are
+ *            non-negative multiples of 8 elements; the runs must not overlap
+ *            and must lie inside the caller's buffer for every slot below
+ *            num_blocks * block_size (not checked: device memory).
+ *   Other arguments as nrc_context_kv_store.
+ * The contiguous [num_blocks, H, block_size, 128] cache of nrc_context_kv_store
+ * is block_stride = H * block_size * 128, page_stride = 128, head_stride =
+ * block_size * 128. Errors: as nrc_context_kv_store, plus NRC_EINVAL (NULL
+ * rows array, rows[l] outside [0, T], negative stride) and NRC_ENOTSUP
+ * (a cache stride not a multiple of 8 elements).
+ */
+int32_t nrc_context_kv_store_ex(const uint16_t* k, const uint16_t* v, int64_t k_layer_stride, int64_t k_row_stride,
+                                int64_t v_layer_stride, int64_t v_row_stride, const int64_t* positions,
+                                const int64_t* const* slots, const int64_t* rows, int64_t T,
+                                const uint16_t* cos_sin, int64_t max_position, uint16_t* const* caches,
+                                int64_t num_blocks, int64_t block_size, int64_t block_stride, int64_t page_stride,
+                                int64_t head_stride, int32_t H, int32_t L, float eps, void* stream);
+
+/*
  * nrc_check_scalars - diagnostic: the device primitives every kernel uses,
  * applied elementwise to n FP32 values (device arrays), so that they can be
  * compared with a reference over all 2^32 inputs:

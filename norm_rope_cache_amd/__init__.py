@@ -73,6 +73,9 @@ def _load():
     L.nrc_context_norms_ex.restype = _i32
     L.nrc_context_norms_ex.argtypes = [_vp, _i64, _i64, _vp, _i32, _vp, _i32, _i32, _f32, _f32, _f32, _f32,
                                        ctypes.c_uint32, _vp, _vp]
+    L.nrc_context_kv_store_ex.restype = _i32
+    L.nrc_context_kv_store_ex.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
+                                          _i64, _i64, _i64, _i64, _i64, _i32, _i32, _f32, _vp]
     L.nrc_context_kv_project.restype = _i32
     L.nrc_context_kv_project.argtypes = [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp]
     L.nrc_context_kv_store.restype = _i32
@@ -276,6 +279,67 @@ def kv_views(kv, H):
     L, T, N = kv.shape
     v5 = kv.view(L, T, 2, H, HEAD_DIM)
     return v5[:, :, 0], v5[:, :, 1]
+
+
+def context_kv_store_ex(kv, positions, slots, cos_sin, caches, H, eps=1e-6, k=None, v=None, stream=None):
+    """The store with per-layer slot lists and strided cache views, in place.
+
+    slots   a list of L entries: a contiguous int64 [rows_l] tensor (its
+            first rows_l rows are inserted) or None (the layer stores nothing)
+    caches  a list of L [num_blocks, H, block_size, 128] bf16 views of one
+            shape and stride, unit last stride (any block / head / page
+            strides that are multiples of 8), or None where slots is None
+    Other arguments as context_kv_store."""
+    import torch
+
+    if k is None:
+        _bf16(kv, "kv")
+        k, v = kv_views(kv, H)
+    for name, t in (("k", k), ("v", v)):
+        _bf16(t, name, contiguous=False)
+        if t.dim() != 4 or t.shape[2] != H or t.shape[3] != HEAD_DIM or t.stride(3) != 1 or t.stride(2) != HEAD_DIM:
+            raise ValueError(f"{name} must be an [L, T, H, 64] view with unit last stride and head stride 64")
+    L, T = k.shape[0], k.shape[1]
+    slot_list, cache_list = list(slots), list(caches)
+    if len(slot_list) != L or len(cache_list) != L:
+        raise ValueError("one cache and one slot list (or None) per layer")
+    live = [c for s, c in zip(slot_list, cache_list) if s is not None]
+    if not live:
+        return
+    c0 = live[0]
+    if c0.dim() != 4 or c0.shape[1] != H or c0.shape[3] != 2 * HEAD_DIM or c0.stride(3) != 1:
+        raise ValueError("caches must be [num_blocks, H, block_size, 128] views with unit last stride")
+    for c in live:
+        if c is None or c.dtype != torch.bfloat16 or not c.is_cuda:
+            raise ValueError("every layer with slots needs a bf16 device cache")
+        if c.shape != c0.shape or c.stride() != c0.stride():
+            raise ValueError("all caches must have one shape and one stride")
+    nb, _, bs, _ = c0.shape
+    rows = []
+    for s in slot_list:
+        if s is None:
+            rows.append(0)
+            continue
+        if s.dtype != torch.int64 or s.dim() != 1 or not s.is_contiguous():
+            raise ValueError("slots must be contiguous int64 [rows] tensors")
+        rows.append(s.shape[0])
+    if cos_sin is not None:
+        _bf16(cos_sin, "cos_sin")
+        if cos_sin.dim() != 2 or cos_sin.shape[1] != HEAD_DIM:
+            raise ValueError("cos_sin must be [max_position, 64]")
+        if positions is None or positions.dtype != torch.int64 or not positions.is_contiguous():
+            raise ValueError("positions must be a contiguous int64 tensor")
+        if positions.shape[0] < max(rows):
+            raise ValueError("positions shorter than the inserted rows")
+    slot_arr = (_vp * L)(*[None if s is None else s.data_ptr() for s in slot_list])
+    cache_arr = (_vp * L)(*[None if (s is None or c is None) else c.data_ptr()
+                            for s, c in zip(slot_list, cache_list)])
+    row_arr = (ctypes.c_int64 * L)(*rows)
+    max_pos = 0 if cos_sin is None else cos_sin.shape[0]
+    _check(_load().nrc_context_kv_store_ex(
+        _ptr(k), _ptr(v), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
+        _ptr(positions) if cos_sin is not None else None, slot_arr, row_arr, T, _ptr(cos_sin), max_pos, cache_arr,
+        nb, bs, c0.stride(0), c0.stride(2), c0.stride(1), H, L, eps, _stream(stream)))
 
 
 def context_kv_store(kv, positions, slots, cos_sin, caches, H, eps=1e-6, rows=None, k=None, v=None,

@@ -13,6 +13,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <vector>
+
 #include "../../include/nrc.h"
 #include "kernels.h"
 
@@ -165,43 +167,59 @@ int32_t nrc_context_kv_project(const uint16_t* normed, const uint16_t* w, uint16
     return launch_status(nrc::launch_kv_project(a, (hipStream_t)stream), "context_kv_project");
 }
 
-int32_t nrc_context_kv_store(const uint16_t* k, const uint16_t* v, int64_t k_layer_stride, int64_t k_row_stride,
-                             int64_t v_layer_stride, int64_t v_row_stride, const int64_t* positions,
-                             const int64_t* const* slots, int64_t rows, int64_t T, const uint16_t* cos_sin,
-                             int64_t max_position, uint16_t* const* caches, int64_t num_blocks, int64_t block_size,
-                             int32_t H, int32_t L, float eps, void* stream) {
-    if (L < 1) return fail(NRC_EINVAL, "context_kv_store: L = %d < 1", L);
-    if (H < 1) return fail(NRC_EINVAL, "context_kv_store: H = %d < 1", H);
-    if (H & (H - 1)) return fail(NRC_ENOTSUP, "context_kv_store: %d KV heads, not a power of two", H);
-    if (T < 0 || rows < 0 || rows > T)
-        return fail(NRC_EINVAL, "context_kv_store: rows = %lld must lie in [0, T = %lld]", (long long)rows,
-                    (long long)T);
-    if (num_blocks < 1 || block_size < 1)
-        return fail(NRC_EINVAL, "context_kv_store: num_blocks and block_size must be >= 1");
+}  // extern "C"
+
+namespace {
+
+// The store behind both entry points: per-layer slot lists (NULL: the layer
+// stores nothing) of rows[l] entries, and a strided cache view.
+int32_t store_impl(const char* what, const uint16_t* k, const uint16_t* v, int64_t k_layer_stride,
+                   int64_t k_row_stride, int64_t v_layer_stride, int64_t v_row_stride, const int64_t* positions,
+                   const int64_t* const* slots, const int64_t* rows, int64_t T, const uint16_t* cos_sin,
+                   int64_t max_position, uint16_t* const* caches, int64_t num_blocks, int64_t block_size,
+                   int64_t block_stride, int64_t page_stride, int64_t head_stride, int32_t H, int32_t L, float eps,
+                   void* stream) {
+    if (L < 1) return fail(NRC_EINVAL, "%s: L = %d < 1", what, L);
+    if (H < 1) return fail(NRC_EINVAL, "%s: H = %d < 1", what, H);
+    if (H & (H - 1)) return fail(NRC_ENOTSUP, "%s: %d KV heads, not a power of two", what, H);
+    if (T < 0) return fail(NRC_EINVAL, "%s: T = %lld < 0", what, (long long)T);
+    if (num_blocks < 1 || block_size < 1) return fail(NRC_EINVAL, "%s: num_blocks and block_size must be >= 1", what);
     if (num_blocks > (((int64_t)1 << 31) - 1) / block_size)
-        return fail(NRC_ENOTSUP, "context_kv_store: %lld x %lld slots do not fit 31 bits", (long long)num_blocks,
+        return fail(NRC_ENOTSUP, "%s: %lld x %lld slots do not fit 31 bits", what, (long long)num_blocks,
                     (long long)block_size);
-    if (rows * H > ((int64_t)1 << 25))
-        return fail(NRC_ENOTSUP, "context_kv_store: rows x heads = %lld too large for one call",
-                    (long long)(rows * H));
-    if (rows == 0) return NRC_OK;
-    if (!k || !v || !slots || !caches) return fail(NRC_EINVAL, "context_kv_store: NULL operand");
-    if (!aligned(k, 16) || !aligned(v, 16))
-        return fail(NRC_EINVAL, "context_kv_store: k and v must be 16-byte aligned");
+    if (!slots || !caches || !rows) return fail(NRC_EINVAL, "%s: NULL slots, rows or caches array", what);
+    int64_t max_rows = 0;
+    for (int32_t l = 0; l < L; ++l) {
+        if (!slots[l]) continue;
+        if (rows[l] < 0 || rows[l] > T)
+            return fail(NRC_EINVAL, "%s: layer %d: rows = %lld must lie in [0, T = %lld]", what, l, (long long)rows[l],
+                        (long long)T);
+        if (rows[l] > max_rows) max_rows = rows[l];
+    }
+    if (max_rows * H > ((int64_t)1 << 25))
+        return fail(NRC_ENOTSUP, "%s: rows x heads = %lld too large for one call", what, (long long)(max_rows * H));
+    if (max_rows == 0) return NRC_OK;
+    if (!k || !v) return fail(NRC_EINVAL, "%s: NULL k or v", what);
+    if (!aligned(k, 16) || !aligned(v, 16)) return fail(NRC_EINVAL, "%s: k and v must be 16-byte aligned", what);
     if ((k_layer_stride | k_row_stride | v_layer_stride | v_row_stride) & 7)
-        return fail(NRC_EINVAL, "context_kv_store: k/v strides must be multiples of 8 elements");
+        return fail(NRC_EINVAL, "%s: k/v strides must be multiples of 8 elements", what);
     if (k_layer_stride < 0 || k_row_stride < 0 || v_layer_stride < 0 || v_row_stride < 0)
-        return fail(NRC_EINVAL, "context_kv_store: negative stride");
+        return fail(NRC_EINVAL, "%s: negative stride", what);
+    if (block_stride < 0 || page_stride < 0 || head_stride < 0)
+        return fail(NRC_EINVAL, "%s: negative cache stride", what);
+    if ((block_stride | page_stride | head_stride) & 7)
+        return fail(NRC_ENOTSUP, "%s: cache strides must be multiples of 8 elements (16-byte accesses)", what);
     if (cos_sin) {
-        if (!positions) return fail(NRC_EINVAL, "context_kv_store: RoPE needs positions");
-        if (max_position < 1) return fail(NRC_EINVAL, "context_kv_store: max_position < 1");
+        if (!positions) return fail(NRC_EINVAL, "%s: RoPE needs positions", what);
+        if (max_position < 1) return fail(NRC_EINVAL, "%s: max_position < 1", what);
         if (!aligned(cos_sin, 16) || !aligned(positions, 8))
-            return fail(NRC_EINVAL, "context_kv_store: cos_sin must be 16-byte, positions 8-byte aligned");
+            return fail(NRC_EINVAL, "%s: cos_sin must be 16-byte, positions 8-byte aligned", what);
     }
     for (int32_t l = 0; l < L; ++l) {
-        if (!slots[l] || !caches[l]) return fail(NRC_EINVAL, "context_kv_store: NULL slots or cache of layer %d", l);
+        if (!slots[l]) continue;
+        if (!caches[l]) return fail(NRC_EINVAL, "%s: NULL cache of layer %d", what, l);
         if (!aligned(slots[l], 8) || !aligned(caches[l], 16))
-            return fail(NRC_EINVAL, "context_kv_store: layer %d: slots must be 8-byte, cache 16-byte aligned", l);
+            return fail(NRC_EINVAL, "%s: layer %d: slots must be 8-byte, cache 16-byte aligned", what, l);
     }
 
     const uint32_t bs = (uint32_t)block_size;
@@ -225,23 +243,70 @@ int32_t nrc_context_kv_store(const uint16_t* k, const uint16_t* v, int64_t k_lay
         a.positions = positions;
         a.cos_sin = cos_sin;
         a.max_position = cos_sin ? max_position : 0;
+        uint32_t launch_rows = 0;
         for (int32_t i = 0; i < nrc::kMaxLayersPerLaunch; ++i) {
-            const int32_t l = first + (i < n ? i : 0);
-            a.layers.cache[i] = caches[l];
-            a.layers.slots[i] = slots[l];
+            const int32_t l = first + i;
+            const bool live = i < n && slots[l] != nullptr;
+            // a layer that stores nothing keeps 0 rows (its pointers are never read)
+            a.layers.cache[i] = live ? caches[l] : nullptr;
+            a.layers.slots[i] = live ? slots[l] : nullptr;
+            a.layers.rows[i] = live ? (uint32_t)rows[l] : 0u;
+            if (a.layers.rows[i] > launch_rows) launch_rows = a.layers.rows[i];
         }
+        if (launch_rows == 0) continue;
         a.layers_in_launch = (uint32_t)n;
-        a.rows = (uint32_t)rows;
+        a.rows = launch_rows;
         a.H = (uint32_t)H;
         a.log2H = log2H;
         a.block_size = bs;
         a.bs_shift = bs_shift;
         a.n_slots = (uint32_t)(num_blocks * block_size);
+        a.block_stride = block_stride;
+        a.page_stride = page_stride;
+        a.head_stride = head_stride;
         a.eps = eps;
-        const int st = launch_status(nrc::launch_kv_store(a, (hipStream_t)stream), "context_kv_store");
+        const int st = launch_status(nrc::launch_kv_store(a, (hipStream_t)stream), what);
         if (st) return st;
     }
     return NRC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t nrc_context_kv_store(const uint16_t* k, const uint16_t* v, int64_t k_layer_stride, int64_t k_row_stride,
+                             int64_t v_layer_stride, int64_t v_row_stride, const int64_t* positions,
+                             const int64_t* const* slots, int64_t rows, int64_t T, const uint16_t* cos_sin,
+                             int64_t max_position, uint16_t* const* caches, int64_t num_blocks, int64_t block_size,
+                             int32_t H, int32_t L, float eps, void* stream) {
+    if (L < 1) return fail(NRC_EINVAL, "context_kv_store: L = %d < 1", L);
+    if (T < 0 || rows < 0 || rows > T)
+        return fail(NRC_EINVAL, "context_kv_store: rows = %lld must lie in [0, T = %lld]", (long long)rows,
+                    (long long)T);
+    if (rows > 0 && (!slots || !caches)) return fail(NRC_EINVAL, "context_kv_store: NULL operand");
+    if (rows > 0)
+        for (int32_t l = 0; l < L; ++l)
+            if (!slots[l] || !caches[l])
+                return fail(NRC_EINVAL, "context_kv_store: NULL slots or cache of layer %d", l);
+    // contiguous [num_blocks, H, block_size, 128] caches, one row count for every layer
+    const int64_t hs = block_size * 2 * NRC_HEAD_DIM;
+    std::vector<int64_t> per_layer((size_t)L, rows);
+    static const int64_t* const none[1] = {nullptr};
+    return store_impl("context_kv_store", k, v, k_layer_stride, k_row_stride, v_layer_stride, v_row_stride, positions,
+                      rows > 0 ? slots : none, per_layer.data(), T, cos_sin, max_position, caches, num_blocks, block_size,
+                      (int64_t)H * hs, 2 * NRC_HEAD_DIM, hs, H, rows > 0 ? L : 1, eps, stream);
+}
+
+int32_t nrc_context_kv_store_ex(const uint16_t* k, const uint16_t* v, int64_t k_layer_stride, int64_t k_row_stride,
+                                int64_t v_layer_stride, int64_t v_row_stride, const int64_t* positions,
+                                const int64_t* const* slots, const int64_t* rows, int64_t T,
+                                const uint16_t* cos_sin, int64_t max_position, uint16_t* const* caches,
+                                int64_t num_blocks, int64_t block_size, int64_t block_stride, int64_t page_stride,
+                                int64_t head_stride, int32_t H, int32_t L, float eps, void* stream) {
+    return store_impl("context_kv_store_ex", k, v, k_layer_stride, k_row_stride, v_layer_stride, v_row_stride,
+                      positions, slots, rows, T, cos_sin, max_position, caches, num_blocks, block_size, block_stride,
+                      page_stride, head_stride, H, L, eps, stream);
 }
 
 int32_t nrc_check_scalars(const float* in, uint16_t* bf16_out, float* rsqrt_out, int64_t n, void* stream) {

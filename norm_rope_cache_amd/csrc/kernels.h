@@ -12,6 +12,7 @@ constexpr int kMaxLayersPerLaunch = 8;
 struct StoreLayers {
     uint16_t* cache[kMaxLayersPerLaunch];
     const int64_t* slots[kMaxLayersPerLaunch];
+    uint32_t rows[kMaxLayersPerLaunch];  // rows inserted per layer (0: the layer stores nothing)
 };
 
 struct KvStoreArgs {
@@ -28,6 +29,7 @@ struct KvStoreArgs {
     uint32_t log2H;
     uint32_t block_size;
     int32_t bs_shift;  // log2(block_size), or -1 when not a power of two
+    int64_t block_stride, page_stride, head_stride;  // cache view strides, elements
     uint32_t n_slots;
     float eps;
 };

@@ -12,7 +12,10 @@
 //
 // Work unit u = (layer, row, head) with the head fastest; lanes 8u .. 8u+7.
 // Rows whose slot is negative (or out of range, or whose position is out of
-// range) read nothing and write nothing.
+// range), and rows past their layer's slot list, read nothing and write
+// nothing. The cache is a strided view: (block, page, head) at block *
+// block_stride + page * page_stride + head * head_stride, K in the first 64
+// elements of the 128-element run and V in the next 64.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -25,7 +28,8 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restric
                                                        const uint16_t* __restrict__ cos_sin, int64_t max_position,
                                                        StoreLayers layers, uint32_t rows, uint32_t H,
                                                        uint32_t log2H, uint32_t total_units, uint32_t block_size,
-                                                       int32_t bs_shift, uint32_t n_slots, float eps) {
+                                                       int32_t bs_shift, uint32_t n_slots, int64_t block_stride,
+                                                       int64_t page_stride, int64_t head_stride, float eps) {
     const uint32_t unit = (blockIdx.x * blockDim.x + threadIdx.x) >> 3;
     const uint32_t g = threadIdx.x & 7u;  // this lane's 8 elements of the head: 8g .. 8g+7
     if (unit >= total_units) return;  // whole 8-lane groups leave together
@@ -34,6 +38,7 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restric
     const uint32_t l = rt / rows;
     const uint32_t t = rt - l * rows;
 
+    if (t >= layers.rows[l]) return;  // past this layer's slot list (or a layer without one)
     const int64_t slot = layers.slots[l][t];
     if (slot < 0 || (uint64_t)slot >= (uint64_t)n_slots) return;
     const uint16_t* cs = nullptr;
@@ -104,7 +109,8 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restric
         block = s32 / block_size;
         page = s32 - block * block_size;
     }
-    uint16_t* dst = layers.cache[l] + ((((int64_t)block * H + h) * block_size + page) * (2 * kHeadDim)) + 8 * g;
+    uint16_t* dst = layers.cache[l] + (int64_t)block * block_stride + (int64_t)page * page_stride +
+                    (int64_t)h * head_stride + 8 * g;
     // Non-temporal: the cache rows are scattered and not read back by this
     // chain, so they go out to HBM now instead of lingering dirty in the
     // caches until the next kernel's traffic evicts them.
@@ -119,11 +125,13 @@ int launch_kv_store(const KvStoreArgs& a, hipStream_t stream) {
     if (a.cos_sin)
         hipLaunchKernelGGL(kv_store_kernel<true>, dim3(blocks), dim3(threads), 0, stream, a.k, a.v, a.k_ls, a.k_rs,
                            a.v_ls, a.v_rs, a.positions, a.cos_sin, a.max_position, a.layers, a.rows, a.H, a.log2H,
-                           total_units, a.block_size, a.bs_shift, a.n_slots, a.eps);
+                           total_units, a.block_size, a.bs_shift, a.n_slots, a.block_stride, a.page_stride,
+                           a.head_stride, a.eps);
     else
         hipLaunchKernelGGL(kv_store_kernel<false>, dim3(blocks), dim3(threads), 0, stream, a.k, a.v, a.k_ls, a.k_rs,
                            a.v_ls, a.v_rs, a.positions, a.cos_sin, a.max_position, a.layers, a.rows, a.H, a.log2H,
-                           total_units, a.block_size, a.bs_shift, a.n_slots, a.eps);
+                           total_units, a.block_size, a.bs_shift, a.n_slots, a.block_stride, a.page_stride,
+                           a.head_stride, a.eps);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -51,6 +51,10 @@ def lib():
         L.nrc_oracle_context_norms_ex.restype = _i32
         L.nrc_oracle_context_norms_ex.argtypes = [_u16p, _i64, _i64, ctypes.c_void_p, _i32, ctypes.c_void_p, _i32, _i32,
                                                   _f32, _f32, _f32, _f32, _i32, _u16p]
+        L.nrc_oracle_context_kv_store_ex.restype = _i32
+        L.nrc_oracle_context_kv_store_ex.argtypes = [
+            _u16p, _i32, _i64, _i32, _i64p, ctypes.POINTER(ctypes.c_void_p), _i64p, _u16p, _i64,
+            ctypes.POINTER(ctypes.c_void_p), _i64p, _i64, _i64, _i64, _i64, _i64, _f32]
         L.nrc_oracle_hidden_norm.argtypes = [_u16p, _i64, _i64, _u16p, _f32, _f32, _f32, _u16p, _f32p]
         L.nrc_oracle_hidden_norm.restype = _i32
         L.nrc_oracle_kv_project.argtypes = [_u16p, _u16p, _f32p, _i32, _i64, _i64, _i64]
@@ -245,6 +249,34 @@ def context_kv_store(kv, H, positions, slots, cos_sin, caches, block_size, eps=1
         _ptr(kv, ctypes.c_uint16), L, T, H, _ptr(positions, ctypes.c_int64), _ptr(slots, ctypes.c_int64), rows,
         _ptr(cs, ctypes.c_uint16), max_pos, _ptr(caches, ctypes.c_uint16), num_blocks, block_size, eps)
     _check(st, "context_kv_store")
+
+
+def context_kv_store_ex(kv, H, positions, slots, cos_sin, caches, block_size, num_blocks, block_stride,
+                        page_stride, head_stride, eps=1e-6):
+    """The store with per-layer slot lists and strided cache views.
+
+    slots: a list of L entries, each an int64 array [rows_l] (rows_l <= T) or
+    None (that layer stores nothing). caches: a list of L flat uint16 arrays,
+    updated in place; element (b, o, h, c) of layer l at b * block_stride +
+    o * page_stride + h * head_stride + c (K in c < 64, V in 64 <= c < 128)."""
+    kv = _c(kv, np.uint16)
+    L, T, N = kv.shape
+    assert N == 2 * H * HEAD_DIM and len(slots) == L and len(caches) == L
+    positions = _c(positions, np.int64)
+    keep = [None if s is None else _c(s, np.int64) for s in slots]
+    sp = (ctypes.c_void_p * L)(*[None if s is None else s.ctypes.data for s in keep])
+    rows = np.array([0 if s is None else s.shape[0] for s in keep], dtype=np.int64)
+    for c in caches:
+        assert c.dtype == np.uint16 and c.ndim == 1 and c.flags.c_contiguous
+    cp = (ctypes.c_void_p * L)(*[c.ctypes.data for c in caches])
+    clen = np.array([c.shape[0] for c in caches], dtype=np.int64)
+    cs = None if cos_sin is None else _c(cos_sin, np.uint16)
+    max_pos = 0 if cs is None else cs.shape[0]
+    st = lib().nrc_oracle_context_kv_store_ex(
+        _ptr(kv, ctypes.c_uint16), L, T, H, _ptr(positions, ctypes.c_int64), sp, _ptr(rows, ctypes.c_int64),
+        _ptr(cs, ctypes.c_uint16), max_pos, cp, _ptr(clen, ctypes.c_int64), num_blocks, block_size, block_stride,
+        page_stride, head_stride, eps)
+    _check(st, "context_kv_store_ex")
 
 
 def chain(x, hidden_w, pre_w, L, w_kv, H, positions, slots, cos_sin, caches, block_size,

@@ -376,6 +376,68 @@ int nrc_oracle_context_kv_store(const uint16_t *kv, int32_t L, int64_t T, int32_
     return status;
 }
 
+/* The store with the pages' full operand surface ([CTX] ContextKvStore,
+ * [RT] ContextKV.store and _slot_groups): per layer l, slots[l] is NULL (the
+ * layer stores nothing) or rows[l] int64 slots (the first rows[l] rows are
+ * inserted); caches[l] points at K of (block 0, page 0, head 0) of a strided
+ * view, element (b, o, h, c) at b * block_stride + o * page_stride +
+ * h * head_stride + c, with K in c < 64 and V in 64 <= c < 128; cache_len[l]
+ * is the number of elements the caller's buffer holds from caches[l] (every
+ * write must fall inside). Other operands as nrc_oracle_context_kv_store. */
+int nrc_oracle_context_kv_store_ex(const uint16_t *kv, int32_t L, int64_t T, int32_t H, const int64_t *positions,
+                                   const int64_t *const *slots, const int64_t *rows, const uint16_t *cos_sin,
+                                   int64_t max_position, uint16_t *const *caches, const int64_t *cache_len,
+                                   int64_t num_blocks, int64_t block_size, int64_t block_stride,
+                                   int64_t page_stride, int64_t head_stride, float eps) {
+    if (L < 1 || T < 0 || H < 1 || num_blocks < 1 || block_size < 1) return ORACLE_EINVAL;
+    const int64_t n_slots = num_blocks * block_size;
+    const int64_t N = 2 * (int64_t)H * HEAD;
+    unsigned char *seen = calloc((size_t)n_slots, 1);
+    if (!seen) return ORACLE_EINVAL;
+    int status = 0;
+    for (int32_t l = 0; l < L && status == 0; ++l) {
+        if (!slots[l]) continue;
+        if (rows[l] < 0 || rows[l] > T) {
+            status = ORACLE_EINVAL;
+            break;
+        }
+        memset(seen, 0, (size_t)n_slots);
+        for (int64_t t = 0; t < rows[l]; ++t) {
+            int64_t s = slots[l][t];
+            if (s < 0) continue;
+            if (s >= n_slots || seen[s]) {
+                status = ORACLE_EINVAL;
+                break;
+            }
+            seen[s] = 1;
+            const uint16_t *cs = NULL;
+            if (cos_sin) {
+                int64_t p = positions[t];
+                if (p < 0 || p >= max_position) {
+                    status = ORACLE_EINVAL;
+                    break;
+                }
+                cs = cos_sin + p * 2 * (HEAD / 2);
+            }
+            const uint32_t page = (uint32_t)s, bs = (uint32_t)block_size;
+            const int64_t b = page / bs, o = page - (uint32_t)b * bs;
+            const uint16_t *row = kv + ((int64_t)l * T + t) * N;
+            for (int32_t h = 0; h < H; ++h) {
+                const int64_t off = b * block_stride + o * page_stride + (int64_t)h * head_stride;
+                if (off < 0 || off + 2 * HEAD > cache_len[l]) {
+                    status = ORACLE_EINVAL;
+                    break;
+                }
+                uint16_t *dst = caches[l] + off;
+                knorm_rope_head(row + (int64_t)h * HEAD, cs, eps, dst);
+                memcpy(dst + HEAD, row + (int64_t)(H + h) * HEAD, HEAD * sizeof(uint16_t));
+            }
+        }
+    }
+    free(seen);
+    return status;
+}
+
 /* The whole chain: norms, projection (rounded to bf16), store. normed
  * [L, T, 8192] and kv [L, T, N] are caller-provided scratch that receive the
  * intermediate results. */

@@ -90,6 +90,36 @@ def test_norms_ex_argument_checks(lib):
     assert call(T=0, x=None, out=None) == 0
 
 
+def test_store_ex_argument_checks(lib):
+    f = lib.nrc_context_kv_store_ex
+    P = ctypes.c_void_p
+    slots = (P * 2)(FAKE.value, None)
+    caches = (P * 2)(FAKE.value, None)
+    rows = (ctypes.c_int64 * 2)(8, 0)
+
+    def call(**kw):
+        a = dict(k=FAKE, v=FAKE, kls=1024 * 16, krs=1024, vls=1024 * 16, vrs=1024, pos=FAKE, slots=slots,
+                 rows=rows, T=16, cs=None, maxp=0, caches=caches, nb=64, bs=16, bstr=8 * 16 * 128, pstr=128,
+                 hstr=16 * 128, H=8, L=2)
+        a.update(kw)
+        return f(a["k"], a["v"], a["kls"], a["krs"], a["vls"], a["vrs"], a["pos"], a["slots"], a["rows"], a["T"],
+                 a["cs"], a["maxp"], a["caches"], a["nb"], a["bs"], a["bstr"], a["pstr"], a["hstr"], a["H"], a["L"],
+                 1e-6, None)
+
+    assert call(rows=None) == EINVAL
+    assert call(rows=(ctypes.c_int64 * 2)(17, 0)) == EINVAL     # rows > T
+    assert call(rows=(ctypes.c_int64 * 2)(-1, 0)) == EINVAL
+    assert call(pstr=-128) == EINVAL
+    assert call(hstr=16 * 128 + 4) == ENOTSUP                  # not a multiple of 8 elements
+    assert call(H=6) == ENOTSUP
+    assert call(caches=(P * 2)(None, None)) == EINVAL          # a storing layer without a cache
+    assert call(caches=(P * 2)(MISALIGNED.value, None)) == EINVAL
+    assert call(k=MISALIGNED) == EINVAL
+    # nothing to store: every layer without slots, or zero rows
+    assert call(slots=(P * 2)(None, None), k=None, v=None) == 0
+    assert call(rows=(ctypes.c_int64 * 2)(0, 5), k=None, v=None) == 0
+
+
 def test_project_argument_checks(lib):
     f = lib.nrc_context_kv_project
     assert f(FAKE, FAKE, FAKE, 0, 8, 8192, 1024, None) == EINVAL

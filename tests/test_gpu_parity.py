@@ -314,6 +314,67 @@ def test_project_one_hot_and_zero_rows(nrc, oracle):
         assert np.all(C[l, T - 10:] == 0)
 
 
+# -------------------------------------------------- store: full operand surface
+
+@pytest.mark.parametrize("layout", ["head-major padded", "page-major", "backend contiguous"])
+def test_store_ex_strided_views_and_slot_groups(nrc, oracle, layout):
+    """Per-layer slot lists of their own lengths, None layers (no store),
+    more than 8 layers (two launches) and strided cache views: every element
+    of each layer's flat buffer (padding included) equals the oracle's."""
+    import torch
+    from norm_rope_cache_amd import synth
+
+    L, T, H, bs, nb = 10, 40, 4, 8, 24
+    N = 2 * H * 64
+    rng = np.random.default_rng(33)
+    kv = synth.normal_bf16(3301, (L, T, N), 0.0, 1.5)
+    pos = rng.integers(0, 128, T).astype(np.int64)
+    tab = synth.to_bf16_bits(rng.uniform(-1, 1, (128, 64)))
+    lens = [40, 0, 17, None, 40, 5, None, 33, 40, 1]
+    slots = []
+    for l, n in enumerate(lens):
+        if n is None:
+            slots.append(None)
+            continue
+        sl = rng.permutation(nb * bs)[:n].astype(np.int64)
+        sl[rng.random(n) < 0.2] = -1
+        slots.append(sl)
+    bstr, pstr, hstr = {"head-major padded": (H * bs * 136 + 64, 136, bs * 136),
+                        "page-major": (bs * H * 128, H * 128, 128),
+                        "backend contiguous": (H * bs * 128, 128, bs * 128)}[layout]
+    size = (nb - 1) * bstr + (bs - 1) * pstr + (H - 1) * hstr + 128
+    prior = [synth.random_bits_u16(3400 + l, (size,)) for l in range(L)]
+    want = [p.copy() for p in prior]
+    oracle.context_kv_store_ex(kv, H, pos, slots, tab, want, bs, nb, bstr, pstr, hstr, 1e-6)
+    flats = [to_dev(p) for p in prior]
+    views = [torch.as_strided(f, (nb, H, bs, 128), (bstr, hstr, pstr, 1)) for f in flats]
+    _say(f"store_ex {layout}")
+    nrc.context_kv_store_ex(to_dev(kv), to_dev(pos), [None if sl is None else to_dev(sl) for sl in slots],
+                            to_dev(tab), [v if sl is not None else None for v, sl in zip(views, slots)], H, 1e-6)
+    torch.cuda.synchronize()
+    for l in range(L):
+        assert_bits_equal(to_host(flats[l]), want[l], f"store_ex {layout} layer {l}")
+
+
+def test_store_ex_matches_store_on_contiguous_caches(nrc):
+    """The general entry on contiguous caches with one slot length is the
+    plain store (same kernel, same bits)."""
+    import torch
+    from norm_rope_cache_amd import synth
+
+    cfg = synth.scaled(synth.PREFILL, 300)
+    d = synth.make_inputs(cfg, with_cache=True, kv_synth=True, with_x=False, with_weights=False)
+    a = to_dev(d["caches"])
+    b = to_dev(d["caches"])
+    kv, pos, cs = to_dev(d["kv"]), to_dev(d["positions"]), to_dev(d["cos_sin"])
+    slots = to_dev(d["slots"])
+    nrc.context_kv_store(kv, pos, slots, cs, a, cfg.H, d["k_eps"])
+    nrc.context_kv_store_ex(kv, pos, [slots[l] for l in range(cfg.L)], cs, [b[l] for l in range(cfg.L)], cfg.H,
+                            d["k_eps"])
+    torch.cuda.synchronize()
+    assert_bits_equal(to_host(b), to_host(a), "store_ex vs store")
+
+
 # -------------------------------------------------------------------- store
 
 def _store_case(name, T=None, kv_rows=4096):

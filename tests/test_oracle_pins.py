@@ -692,6 +692,55 @@ def test_insert_brute_force_tiny(oracle):
                     assert np.array_equal(cell[64:], kv[l, t, (H + h) * 64:(H + h + 1) * 64])
 
 
+def test_insert_strided_views_and_slot_groups_brute_force(oracle):
+    """The store's full operand surface (context page ContextKvStore: a
+    strided key-cache view; runtime page _slot_groups: per-layer slot lists
+    of their own lengths, None for a layer that stores nothing). Brute force
+    over every cell of padded strided buffers: a cell holds the (row, head)
+    whose slot maps to it among the layer's first rows_l rows (K-norm + RoPE
+    of K by the pinned head routine, V copied) or keeps its prior bits; the
+    padding between runs is never written; a None layer is untouched."""
+    rng = np.random.default_rng(17)
+    L, T, H, bs, nb = 3, 12, 2, 4, 5
+    N = 2 * H * 64
+    kv = bf16_bits_of(rng.standard_normal((L, T, N)) * 1.8)
+    pos = rng.integers(0, 64, T).astype(np.int64)
+    tab = bf16_bits_of(rng.uniform(-1, 1, (64, 64)))
+    slots = [rng.permutation(nb * bs)[:10].astype(np.int64), None, rng.permutation(nb * bs)[:7].astype(np.int64)]
+    slots[0][3] = -1
+    slots[2][0] = -5
+    layouts = {
+        # backend layout [nb, H, bs, 128] with 8 spare elements after every run and 64 after every block
+        "head-major padded": (H * bs * 136 + 64, 136, bs * 136),
+        # [nb, bs, H, 128] (page-major) with no padding
+        "page-major": (bs * H * 128, H * 128, 128),
+    }
+    for name, (bstr, pstr, hstr) in layouts.items():
+        size = (nb - 1) * bstr + (bs - 1) * pstr + (H - 1) * hstr + 128
+        prior = [rng.integers(0, 1 << 16, size).astype(np.uint16) for _ in range(L)]
+        caches = [p.copy() for p in prior]
+        oracle.context_kv_store_ex(kv, H, pos, slots, tab, caches, bs, nb, bstr, pstr, hstr, 1e-6)
+        for l in range(L):
+            written = np.zeros(size, dtype=bool)
+            for b in range(nb):
+                for o in range(bs):
+                    for h in range(H):
+                        off = b * bstr + o * pstr + h * hstr
+                        cell = caches[l][off:off + 128]
+                        sl = slots[l]
+                        writers = [] if sl is None else [t for t in range(sl.shape[0]) if sl[t] >= 0
+                                                         and sl[t] // bs == b and sl[t] % bs == o]
+                        if not writers:
+                            assert np.array_equal(cell, prior[l][off:off + 128]), (name, l, b, o, h)
+                            continue
+                        (t,) = writers
+                        written[off:off + 128] = True
+                        kh = kv[l, t, h * 64:(h + 1) * 64]
+                        assert np.array_equal(cell[:64], oracle.knorm_rope_head(kh, tab[pos[t]], 1e-6))
+                        assert np.array_equal(cell[64:], kv[l, t, (H + h) * 64:(H + h + 1) * 64])
+            assert np.array_equal(caches[l][~written], prior[l][~written]), (name, l)
+
+
 def test_insert_preconditions(oracle):
     L, T, H, bs, nb = 1, 4, 1, 4, 2
     kv = np.zeros((L, T, 128), dtype=np.uint16)
