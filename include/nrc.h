@@ -119,6 +119,23 @@ int32_t nrc_context_norms_ex(const uint16_t* x, int64_t T, int64_t D, const void
 int32_t nrc_context_kv_project(const uint16_t* normed, const uint16_t* w, uint16_t* kv, int32_t L, int64_t T,
                                int64_t D, int64_t N, void* stream);
 
+/* Weight layouts of nrc_context_kv_project_ex. */
+#define NRC_KV_WEIGHT_DN 0 /* [L, D, N], N contiguous (the bmm's logical right operand) */
+#define NRC_KV_WEIGHT_ND 1 /* [L, N, D], D contiguous (the pages' stacked weight storage) */
+
+/*
+ * nrc_context_kv_project_ex - nrc_context_kv_project with the weight in
+ * either layout. Page "...runtime.draft", ContextKV._project: the pages
+ * stack the layers' K/V weights as [L, N, D] and multiply by its transpose.
+ *
+ *   w_layout  NRC_KV_WEIGHT_DN: w is [L, D, N]; NRC_KV_WEIGHT_ND: w is
+ *             [L, N, D]; contiguous, 16-byte aligned.
+ *   Other arguments and errors as nrc_context_kv_project, plus NRC_EINVAL
+ *   for an unknown layout. Both layouts give the same bits.
+ */
+int32_t nrc_context_kv_project_ex(const uint16_t* normed, const uint16_t* w, int32_t w_layout, uint16_t* kv,
+                                  int32_t L, int64_t T, int64_t D, int64_t N, void* stream);
+
 /*
  * nrc_context_hidden_norm - the pre-pass of the fused norms + projection: the
  * hidden norm and each row's layer-norm scale, the two quantities every

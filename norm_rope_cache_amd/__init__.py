@@ -76,6 +76,8 @@ def _load():
     L.nrc_context_kv_store_ex.restype = _i32
     L.nrc_context_kv_store_ex.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
                                           _i64, _i64, _i64, _i64, _i64, _i32, _i32, _f32, _vp]
+    L.nrc_context_kv_project_ex.restype = _i32
+    L.nrc_context_kv_project_ex.argtypes = [_vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp]
     L.nrc_context_kv_project.restype = _i32
     L.nrc_context_kv_project.argtypes = [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp]
     L.nrc_context_kv_store.restype = _i32
@@ -254,23 +256,35 @@ def context_kv_project_fused(h, r, pre_w, w_kv, pre_center=0.0, out=None, stream
     return out
 
 
-def context_kv_project(normed, w_kv, out=None, stream=None):
-    """[L, T, D] x [L, D, N] -> [L, T, N] bf16 (FP32 accumulation)."""
+def context_kv_project(normed, w_kv, out=None, stream=None, w_layout="dn"):
+    """[L, T, D] x [L, D, N] -> [L, T, N] bf16 (FP32 accumulation).
+    w_layout "nd": w_kv is stored [L, N, D] (the pages' storage)."""
     import torch
 
     _bf16(normed, "normed")
     _bf16(w_kv, "w_kv")
     L, T, D = normed.shape
-    if w_kv.dim() != 3 or w_kv.shape[0] != L or w_kv.shape[1] != D:
-        raise ValueError("w_kv must be [L, D, N]")
-    N = w_kv.shape[2]
+    if w_layout == "dn":
+        if w_kv.dim() != 3 or w_kv.shape[0] != L or w_kv.shape[1] != D:
+            raise ValueError("w_kv must be [L, D, N]")
+        N = w_kv.shape[2]
+    elif w_layout == "nd":
+        if w_kv.dim() != 3 or w_kv.shape[0] != L or w_kv.shape[2] != D:
+            raise ValueError("w_kv must be [L, N, D]")
+        N = w_kv.shape[1]
+    else:
+        raise ValueError("w_layout is 'dn' or 'nd'")
     if out is None:
         out = torch.empty((L, T, N), dtype=torch.bfloat16, device=normed.device)
     else:
         _bf16(out, "out")
         if tuple(out.shape) != (L, T, N):
             raise ValueError("out must be [L, T, N]")
-    _check(_load().nrc_context_kv_project(_ptr(normed), _ptr(w_kv), _ptr(out), L, T, D, N, _stream(stream)))
+    if w_layout == "dn":
+        _check(_load().nrc_context_kv_project(_ptr(normed), _ptr(w_kv), _ptr(out), L, T, D, N, _stream(stream)))
+    else:
+        _check(_load().nrc_context_kv_project_ex(_ptr(normed), _ptr(w_kv), 1, _ptr(out), L, T, D, N,
+                                                 _stream(stream)))
     return out
 
 

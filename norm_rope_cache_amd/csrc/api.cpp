@@ -147,8 +147,10 @@ int32_t nrc_context_kv_project_fused(const uint16_t* h, const float* r, const ui
                          "context_kv_project_fused");
 }
 
-int32_t nrc_context_kv_project(const uint16_t* normed, const uint16_t* w, uint16_t* kv, int32_t L, int64_t T,
-                               int64_t D, int64_t N, void* stream) {
+int32_t nrc_context_kv_project_ex(const uint16_t* normed, const uint16_t* w, int32_t w_layout, uint16_t* kv,
+                                  int32_t L, int64_t T, int64_t D, int64_t N, void* stream) {
+    if (w_layout != NRC_KV_WEIGHT_DN && w_layout != NRC_KV_WEIGHT_ND)
+        return fail(NRC_EINVAL, "context_kv_project: weight layout %d (0 [L, D, N], 1 [L, N, D])", w_layout);
     if (L < 1) return fail(NRC_EINVAL, "context_kv_project: L = %d < 1", L);
     if (T < 0) return fail(NRC_EINVAL, "context_kv_project: T = %lld < 0", (long long)T);
     if (D <= 0 || D % 64) return fail(NRC_ENOTSUP, "context_kv_project: D = %lld is not a positive multiple of 64",
@@ -164,7 +166,13 @@ int32_t nrc_context_kv_project(const uint16_t* normed, const uint16_t* w, uint16
     if (!aligned(normed, 16) || !aligned(w, 16) || !aligned(kv, 16))
         return fail(NRC_EINVAL, "context_kv_project: operands must be 16-byte aligned");
     nrc::ProjectArgs a{normed, w, kv, L, T, D, N, num_cus()};
+    a.b_nd = w_layout == NRC_KV_WEIGHT_ND;
     return launch_status(nrc::launch_kv_project(a, (hipStream_t)stream), "context_kv_project");
+}
+
+int32_t nrc_context_kv_project(const uint16_t* normed, const uint16_t* w, uint16_t* kv, int32_t L, int64_t T,
+                               int64_t D, int64_t N, void* stream) {
+    return nrc_context_kv_project_ex(normed, w, NRC_KV_WEIGHT_DN, kv, L, T, D, N, stream);
 }
 
 }  // extern "C"

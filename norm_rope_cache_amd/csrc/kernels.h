@@ -70,11 +70,12 @@ int launch_hidden_norm(const NormsArgs& a, uint16_t* h_out, float* r_out, hipStr
 
 struct ProjectArgs {
     const uint16_t* A;  // [L, M, K]
-    const uint16_t* B;  // [L, K, N]
+    const uint16_t* B;  // [L, K, N], or [L, N, K] when b_nd
     uint16_t* C;        // [L, M, N]
     int32_t L;
     int64_t M, K, N;
     int32_t num_cus;
+    bool b_nd = false;
 };
 
 int launch_kv_project(const ProjectArgs& a, hipStream_t stream);

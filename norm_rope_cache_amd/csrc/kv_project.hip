@@ -102,7 +102,10 @@ struct FusedA {
 // tile, layer, N tile, so the layers of one h panel run together).
 // CMODE (fused, with weights): 0 - gamma = w; 1 - gamma = w with -0.0 turned
 // into +0.0 (a +0.0 center); 2 - gamma = w + center in FP32.
-template <int BM, int BN, int WM, int WN, bool FUSED, bool PW, int CMODE>
+// B_ND: the weight is stored [L, N, K] (K contiguous, the pages' storage)
+// instead of [L, K, N]; its tile then takes A's path (64-byte rows per
+// stage, A's swizzle, ds_read_b128 fragments).
+template <int BM, int BN, int WM, int WN, bool FUSED, bool PW, int CMODE, bool B_ND>
 __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t* __restrict__ A,
                                                               const uint16_t* __restrict__ B,
                                                               uint16_t* __restrict__ C, int64_t M, int64_t K,
@@ -172,9 +175,15 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
 #pragma unroll
         for (int t = 0; t < CF::B_LOADS; ++t) {
             const int off = (wave * CF::B_LOADS + t) * 1024 + lane * 16;
-            const int r = off / CF::B_ROW, pc = (off % CF::B_ROW) >> 4;
-            const int c = pc ^ swz_b(r);
-            b_src[t] = Bl + (int64_t)r * N + n0 + 8 * c;
+            if constexpr (B_ND) {
+                const int r = off >> 6, pc = (off >> 4) & 3;
+                const int c = pc ^ swz_a(r);
+                b_src[t] = Bl + (n0 + r) * K + 8 * c;
+            } else {
+                const int r = off / CF::B_ROW, pc = (off % CF::B_ROW) >> 4;
+                const int c = pc ^ swz_b(r);
+                b_src[t] = Bl + (int64_t)r * N + n0 + 8 * c;
+            }
         }
     };
 
@@ -275,6 +284,17 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
         }
     }
 
+    // B stored [L, N, K]: lane reads column row wn BN/WN + 32 j + (lane & 31),
+    // k chunk 2 kk + (lane >> 5), as for A.
+    int bnd_off[2][CF::NI];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int j = 0; j < CF::NI; ++j) {
+            const int r = wn * CF::WTN + 32 * j + (lane & 31);
+            bnd_off[kk][j] = CF::A_REGION + r * 64 + 16 * ((2 * kk + khalf) ^ swz_a(r));
+        }
+
     f32x16 acc[CF::MI][CF::NI];
 
     // ---- one-instruction building blocks of the scheduled loop.
@@ -282,15 +302,25 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     // blocks i, bfr[f][j] for its 32-column blocks j.
     bf16x8 af[2][CF::MI], bfr[2][CF::NI];
     constexpr int NM = CF::MI * CF::NI;      // MFMAs per sub-step
-    constexpr int NR = CF::MI + 2 * CF::NI;  // LDS reads per sub-step
+    constexpr int NR = CF::MI + (B_ND ? 1 : 2) * CF::NI;  // LDS reads per sub-step
     constexpr int HALF = CF::LOADS / 2;      // DMAs issued per sub-step
     static_assert(CF::LOADS % 2 == 0 && HALF <= NM, "DMA spread");
     // LDS read r of sub-step (buf, kk) into set f, in the order the MFMAs
-    // consume them: A0, B0 (two transposing halves), B1, ..., then A1, A2, ..
+    // consume them: A0, B0 (two transposing halves, or one read for the
+    // [L, N, K] storage), B1, ..., then A1, A2, ..
     auto read_one = [&](int buf, int kk, int f, int r) {
         typedef short i16x8 __attribute__((ext_vector_type(8)));
         const lds_char* sa = lds + buf * CF::A_BYTES;
         const lds_char* sb = lds + buf * CF::B_BYTES;
+        if constexpr (B_ND) {
+            if (r == 0 || r > CF::NI) {
+                const int i = r == 0 ? 0 : r - CF::NI;
+                af[f][i] = *(const __attribute__((address_space(3))) bf16x8*)(sa + a_off[kk] + i * 32 * 64);
+            } else {
+                bfr[f][r - 1] = *(const __attribute__((address_space(3))) bf16x8*)(sb + bnd_off[kk][r - 1]);
+            }
+            return;
+        }
         if (r == 0 || r > 2 * CF::NI) {
             const int i = r == 0 ? 0 : r - 2 * CF::NI;
             af[f][i] = *(const __attribute__((address_space(3))) bf16x8*)(sa + a_off[kk] + i * 32 * 64);
@@ -323,7 +353,7 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
                   __builtin_amdgcn_readfirstlane(base + buf * CF::A_BYTES + (wave * CF::A_LOADS + d) * 1024));
         } else {
             const int t = d - CF::A_LOADS;
-            dma16(b_src[t] + (int64_t)s * kBK * N,
+            dma16(b_src[t] + (B_ND ? (int64_t)s * kBK : (int64_t)s * kBK * N),
                   __builtin_amdgcn_readfirstlane(base + CF::A_REGION + buf * CF::B_BYTES +
                                                  (wave * CF::B_LOADS + t) * 1024));
         }
@@ -470,14 +500,14 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     wait_vmcnt<0>();  // no DMA may still target this workgroup's LDS at exit
 }
 
-template <int BM, int BN, int WM, int WN, bool FUSED, bool PW, int CMODE>
+template <int BM, int BN, int WM, int WN, bool FUSED, bool PW, int CMODE, bool B_ND>
 int launch_tiles(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
     using CF = Cfg<BM, BN, WM, WN>;
     const int tiles_m = (int)((a.M + BM - 1) / BM);
     const int tiles_n = (int)(a.N / BN);
     const int total = a.L * tiles_m * tiles_n;
     const size_t lds_bytes = CF::LDS_BYTES + ((FUSED && PW) ? (size_t)a.K * 2 : 0);
-    auto kernel = kv_project_kernel<BM, BN, WM, WN, FUSED, PW, CMODE>;
+    auto kernel = kv_project_kernel<BM, BN, WM, WN, FUSED, PW, CMODE, B_ND>;
     if (lds_bytes > 65536) {
         // The opt-in above 64 KiB is per kernel and device; set it on each device once.
         static int attr_set[64] = {};
@@ -501,19 +531,20 @@ int launch_tiles(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
     return 0;
 }
 
-template <bool FUSED, bool PW, int CMODE>
+template <bool FUSED, bool PW, int CMODE, bool B_ND>
 int launch_shape(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
     // 256 x 256 tiles when they fill the chip, else 128 x 128.
     const int64_t big_tiles = (int64_t)a.L * ((a.M + 255) / 256) * (a.N / 256);
     const int cus = a.num_cus > 0 ? a.num_cus : 256;
-    if (a.N % 256 == 0 && big_tiles >= cus) return launch_tiles<256, 256, 2, 4, FUSED, PW, CMODE>(a, fa, stream);
-    return launch_tiles<128, 128, 2, 2, FUSED, PW, CMODE>(a, fa, stream);
+    if (a.N % 256 == 0 && big_tiles >= cus) return launch_tiles<256, 256, 2, 4, FUSED, PW, CMODE, B_ND>(a, fa, stream);
+    return launch_tiles<128, 128, 2, 2, FUSED, PW, CMODE, B_ND>(a, fa, stream);
 }
 
 }  // namespace
 
 int launch_kv_project(const ProjectArgs& a, hipStream_t stream) {
-    const int rc = launch_shape<false, false, 0>(a, FusedA{nullptr, nullptr, 0.0f}, stream);
+    const int rc = a.b_nd ? launch_shape<false, false, 0, true>(a, FusedA{nullptr, nullptr, 0.0f}, stream)
+                          : launch_shape<false, false, 0, false>(a, FusedA{nullptr, nullptr, 0.0f}, stream);
     if (rc) return rc;
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -523,12 +554,12 @@ int launch_kv_project_fused(const ProjectArgs& a, const float* r, const uint16_t
     const FusedA fa{r, gamma, center};
     int rc;
     if (!gamma)
-        rc = launch_shape<true, false, 0>(a, fa, stream);
+        rc = launch_shape<true, false, 0, false>(a, fa, stream);
     else if (center == 0.0f)
-        rc = __builtin_signbit(center) ? launch_shape<true, true, 0>(a, fa, stream)
-                                       : launch_shape<true, true, 1>(a, fa, stream);
+        rc = __builtin_signbit(center) ? launch_shape<true, true, 0, false>(a, fa, stream)
+                                       : launch_shape<true, true, 1, false>(a, fa, stream);
     else
-        rc = launch_shape<true, true, 2>(a, fa, stream);
+        rc = launch_shape<true, true, 2, false>(a, fa, stream);
     if (rc) return rc;
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -55,6 +55,8 @@ def lib():
         L.nrc_oracle_context_kv_store_ex.argtypes = [
             _u16p, _i32, _i64, _i32, _i64p, ctypes.POINTER(ctypes.c_void_p), _i64p, _u16p, _i64,
             ctypes.POINTER(ctypes.c_void_p), _i64p, _i64, _i64, _i64, _i64, _i64, _f32]
+        L.nrc_oracle_kv_project_nd.restype = _i32
+        L.nrc_oracle_kv_project_nd.argtypes = [_u16p, _u16p, _f32p, _i32, _i64, _i64, _i64]
         L.nrc_oracle_hidden_norm.argtypes = [_u16p, _i64, _i64, _u16p, _f32, _f32, _f32, _u16p, _f32p]
         L.nrc_oracle_hidden_norm.restype = _i32
         L.nrc_oracle_kv_project.argtypes = [_u16p, _u16p, _f32p, _i32, _i64, _i64, _i64]
@@ -211,6 +213,21 @@ def kv_project(A, B):
     st = lib().nrc_oracle_kv_project(_ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16), _ptr(C, ctypes.c_float),
                                      L, T, Dd, N)
     _check(st, "kv_project")
+    return C
+
+
+def kv_project_nd(A, B):
+    """A [L, T, D] bf16 bits, B [L, N, D] bf16 bits (the pages' weight
+    storage) -> C [L, T, N] float32."""
+    A = _c(A, np.uint16)
+    B = _c(B, np.uint16)
+    L, T, Dd = A.shape
+    assert B.shape[0] == L and B.shape[2] == Dd
+    N = B.shape[1]
+    C = np.empty((L, T, N), dtype=np.float32)
+    st = lib().nrc_oracle_kv_project_nd(_ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16),
+                                        _ptr(C, ctypes.c_float), L, T, Dd, N)
+    _check(st, "kv_project_nd")
     return C
 
 

@@ -304,6 +304,26 @@ int nrc_oracle_kv_project(const uint16_t *A, const uint16_t *B, float *C, int32_
     return 0;
 }
 
+/* The same projection with the weight stored as the pages keep it, [L, N, D]
+ * (the bmm's right operand is its transpose, [RT] ContextKV._project):
+ * C[l, t, n] = sum over d in increasing order of A[l, t, d] * B[l, n, d],
+ * FP32. */
+int nrc_oracle_kv_project_nd(const uint16_t *A, const uint16_t *B, float *C, int32_t L, int64_t T, int64_t D,
+                             int64_t N) {
+    if (L < 1 || T < 0 || D < 1 || N < 1 || !A || !B || !C) return ORACLE_EINVAL;
+    for (int32_t l = 0; l < L; ++l)
+        for (int64_t t = 0; t < T; ++t) {
+            const uint16_t *a = A + ((int64_t)l * T + t) * D;
+            for (int64_t n = 0; n < N; ++n) {
+                const uint16_t *b = B + ((int64_t)l * N + n) * D;
+                float c = 0.0f;
+                for (int64_t d = 0; d < D; ++d) c = c + f_of(a[d]) * f_of(b[d]);
+                C[((int64_t)l * T + t) * N + n] = c;
+            }
+        }
+    return 0;
+}
+
 /* One head's K-norm (+ RoPE) as [CTX] _ContextKvStoreKernel computes it:
  * k_in [64] bf16, cs_row [64] bf16 (cos | sin) or NULL, out [64] bf16. */
 void nrc_oracle_knorm_rope_head(const uint16_t *k_in, const uint16_t *cs_row, float eps, uint16_t *out) {

@@ -297,6 +297,28 @@ def test_project_several_tiles_per_workgroup(nrc, oracle, L, T, N):
     _project_check(nrc, oracle, A, B, rows, f"project multi-tile L={L} T={T} N={N}")
 
 
+@pytest.mark.parametrize("L,T,N", [(2, 37, 256), (4, 300, 1024), (1, 513, 384), (4, 16384, 1024)])
+def test_project_nd_weight_layout(nrc, oracle, L, T, N):
+    """The pages' [L, N, D] weight storage: the same bits as the [L, D, N]
+    layout (same sums in the same order), and within tolerance of the
+    oracle's [L, N, D] routine on sampled rows (the last shape is the long
+    workload's launch)."""
+    from norm_rope_cache_amd import synth
+
+    A = synth.normal_bf16(8100 + T, (L, T, 8192))
+    Bnd = synth.normal_bf16(8200 + N, (L, N, 8192), std=0.02)
+    Bdn = np.ascontiguousarray(Bnd.transpose(0, 2, 1))
+    _say(f"project nd L={L} T={T} N={N}")
+    Ad = to_dev(A)
+    c_nd = to_host(nrc.context_kv_project(Ad, to_dev(Bnd), w_layout="nd"))
+    c_dn = to_host(nrc.context_kv_project(Ad, to_dev(Bdn)))
+    assert_bits_equal(c_nd, c_dn, f"nd vs dn L={L} T={T} N={N}")
+    rows = np.unique(np.concatenate([[0, T - 1], np.arange(1, T, max(1, T // 24))]))
+    Cstar = oracle.kv_project_nd(np.ascontiguousarray(A[:, rows]), Bnd)
+    ok, msg = projection_tolerance_ok(c_nd[:, rows], Cstar)
+    assert ok, msg
+
+
 def test_project_one_hot_and_zero_rows(nrc, oracle):
     """A one-hot row selects a row of B: the result is that row's bf16 value
     exactly; an all-zero row gives +0."""

@@ -426,6 +426,29 @@ def test_hidden_norm_pieces_rebuild_the_norms(oracle):
             assert np.array_equal(full[l], want.view(torch.int16).numpy().view(np.uint16)), l
 
 
+def test_projection_nd_layout(oracle):
+    """The [L, N, D] weight storage holds the transpose of the bmm's operand:
+    the same FP32 sums in the same d order, so equal bits to the [L, D, N]
+    routine on the transposed weight; one-hot rows pick B's bf16 rows exactly
+    and zero rows give +0."""
+    rng = np.random.default_rng(51)
+    L, T, Dd, N = 2, 5, 256, 24
+    A = bf16_bits_of(rng.standard_normal((L, T, Dd)))
+    Bnd = bf16_bits_of(rng.standard_normal((L, N, Dd)) * 0.05)
+    got = oracle.kv_project_nd(A, Bnd)
+    want = oracle.kv_project(A, np.ascontiguousarray(Bnd.transpose(0, 2, 1)))
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    oh = np.zeros((L, T, Dd), dtype=np.uint16)
+    cols = [3, 200, 17, 255]
+    for t, c in enumerate(cols):
+        oh[:, t, c] = 0x3F80
+    C = oracle.kv_project_nd(oh, Bnd)
+    for l in range(L):
+        for t, c in enumerate(cols):
+            assert np.array_equal(C[l, t], f32_of_bf16(Bnd[l, :, c]))
+        assert np.all(C[l, len(cols):] == 0) and not np.signbit(C[l, len(cols):]).any()
+
+
 # ------------------------------------------- norm variants (FP32, input scale)
 
 def _bf16_round_indep(f):
