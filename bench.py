@@ -247,6 +247,28 @@ def main():
             name = "context_norms_ex[fp32 weights" + (", input-scaled]" if his else "]")
             variants[name] = {"bound": "hbm", "ms": ms, "bytes": vb, "achieved_GBs": vb / (ms * 1e-3) / 1e9,
                               "frac": vb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        # The residual boundary over the same number of rows: bf16 branch, FP32
+        # stream in and out, bf16 output, bf16 norm weights.
+        s_in = torch.empty((cfg.T, 8192), dtype=torch.float32, device=dev).normal_()
+        alpha = torch.full((8192,), 0.9, dtype=torch.float32, device=dev)
+        beta = torch.full((8192,), 1.1, dtype=torch.float32, device=dev)
+        s_out = torch.empty_like(s_in)
+        b_out = torch.empty((cfg.T, 8192), dtype=torch.bfloat16, device=dev)
+        run = lambda: nrc.draft_boundary(x, s_in, alpha, beta, hw, pw[0], out=b_out, stream_out=s_out)
+        for _ in range(3):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        bb = cfg.T * 8192 * (2 + 4 + 4 + 2) + 8192 * (4 + 4 + 2 + 2)
+        variants["draft_boundary[fp32 stream in/out]"] = {"bound": "hbm", "ms": ms, "bytes": bb,
+                                                         "achieved_GBs": bb / (ms * 1e-3) / 1e9,
+                                                         "frac": bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del s_in, s_out, b_out
         log("variants: " + ", ".join(f"{k}={v['ms']:.4f} ms" for k, v in variants.items()))
 
     cpu = None

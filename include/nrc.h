@@ -71,6 +71,7 @@ int32_t nrc_context_norms(const uint16_t* x, int64_t T, int64_t D, const uint16_
 #define NRC_WEIGHT_NONE 0
 #define NRC_WEIGHT_BF16 1
 #define NRC_WEIGHT_F32 2
+#define NRC_WEIGHT_F16 3 /* nrc_draft_boundary only */
 #define NRC_HIDDEN_INPUT_SCALE 1u
 #define NRC_PRE_INPUT_SCALE 2u
 
@@ -99,6 +100,42 @@ int32_t nrc_context_norms(const uint16_t* x, int64_t T, int64_t D, const uint16_
 int32_t nrc_context_norms_ex(const uint16_t* x, int64_t T, int64_t D, const void* hidden_w, int32_t hidden_kind,
                              const void* pre_w, int32_t pre_kind, int32_t L, float hidden_eps, float pre_eps,
                              float hidden_center, float pre_center, uint32_t flags, uint16_t* out, void* stream);
+
+/* Stream kinds and flags of nrc_draft_boundary. */
+#define NRC_STREAM_F32 0
+#define NRC_STREAM_BF16 1
+#define NRC_POST_INPUT_SCALE 1u
+#define NRC_PRE_INPUT_SCALE 2u
+
+/*
+ * nrc_draft_boundary - one residual boundary of the DSpark draft: post norm
+ * of the bf16 branch, the gated FP32 residual, then the next pre norm.
+ * Page "...cutedsl.common.draft_boundary": module summary,
+ * boundary_fragments, DraftBoundary.run, DraftBoundaryConstants.
+ *
+ *   branch     [m, D] bf16, contiguous, 16-byte aligned; D must be 8192.
+ *   stream_in  [m, D] FP32 (stream_kind NRC_STREAM_F32) or bf16
+ *              (NRC_STREAM_BF16), contiguous, 16-byte aligned.
+ *   alpha, beta  [D] FP32 gates, 16-byte aligned.
+ *   post_w, pre_w  [D] weights of kind NRC_WEIGHT_NONE (NULL), _BF16, _F32
+ *              or _F16; the gain is w + center (FP32 add).
+ *   flags      NRC_POST_INPUT_SCALE / NRC_PRE_INPUT_SCALE: that norm's
+ *              weight scales its input (else its output).
+ *   stream_out [m, D] FP32 new stream, or NULL (not stored).
+ *   out        [m, D] bf16.
+ * Per row: post norm u = x (or gamma_post * x), r1 = 1/sqrt(S(u)/D +
+ * post_eps), y = u * r1 (* gamma_post); res = alpha * stream + beta *
+ * bf16(y) (each product rounded, then the sum), stream_out = res; pre norm of
+ * z = bf16(res) the same way with gamma_pre and pre_eps, rounded to bf16.
+ * Sums in the library's fixed order; bf16 rounding to nearest even, NaN ->
+ * 0x7FC0. m == 0 returns NRC_OK. Errors: NRC_EINVAL (kinds out of range, a
+ * weight pointer against its kind, unknown flags, NULL operands with
+ * m > 0, m < 0, misalignment), NRC_ENOTSUP (D != 8192).
+ */
+int32_t nrc_draft_boundary(const uint16_t* branch, int64_t m, int64_t D, const void* stream_in, int32_t stream_kind,
+                           const float* alpha, const float* beta, const void* post_w, int32_t post_kind,
+                           const void* pre_w, int32_t pre_kind, float post_eps, float pre_eps, float post_center,
+                           float pre_center, uint32_t flags, float* stream_out, uint16_t* out, void* stream);
 
 /*
  * nrc_context_kv_project - the batched K/V projection C[l] = A[l] . B[l].

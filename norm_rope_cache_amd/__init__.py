@@ -78,6 +78,9 @@ def _load():
                                           _i64, _i64, _i64, _i64, _i64, _i32, _i32, _f32, _vp]
     L.nrc_context_kv_project_ex.restype = _i32
     L.nrc_context_kv_project_ex.argtypes = [_vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp]
+    L.nrc_draft_boundary.restype = _i32
+    L.nrc_draft_boundary.argtypes = [_vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _f32, _f32, _f32,
+                                     _f32, ctypes.c_uint32, _vp, _vp, _vp]
     L.nrc_context_kv_project.restype = _i32
     L.nrc_context_kv_project.argtypes = [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp]
     L.nrc_context_kv_store.restype = _i32
@@ -201,6 +204,59 @@ def context_norms_ex(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hidde
     _check(_load().nrc_context_norms_ex(_ptr(x), T, D, _ptr(hidden_w), hk, _ptr(pre_w), pk, L, hidden_eps, pre_eps,
                                         hidden_center, pre_center, flags, _ptr(out), _stream(stream)))
     return out
+
+
+def _boundary_kind(w, name):
+    import torch
+
+    if w is None:
+        return WEIGHT_NONE
+    if not w.is_cuda or not w.is_contiguous() or tuple(w.shape) != (8192,):
+        raise ValueError(f"{name} must be a contiguous device tensor of shape [8192]")
+    kinds = {torch.bfloat16: WEIGHT_BF16, torch.float32: WEIGHT_F32, torch.float16: 3}
+    if w.dtype not in kinds:
+        raise ValueError(f"{name} must be bf16, float32 or float16, not {w.dtype}")
+    return kinds[w.dtype]
+
+
+def draft_boundary(branch, stream_in, alpha, beta, post_w=None, pre_w=None, post_eps=1e-6, pre_eps=1e-6,
+                   post_center=0.0, pre_center=0.0, post_input_scale=False, pre_input_scale=False,
+                   store_stream=True, out=None, stream_out=None, stream=None):
+    """One residual boundary: (new FP32 stream or None, bf16 out [m, 8192]).
+
+    branch [m, 8192] bf16; stream_in [m, 8192] float32 or bf16; alpha, beta
+    float32 [8192]; post_w / pre_w [8192] bf16, float32 or float16 (None:
+    weightless); *_input_scale: that weight scales the norm's input."""
+    import torch
+
+    _bf16(branch, "branch")
+    if branch.dim() != 2:
+        raise ValueError("branch must be [m, 8192]")
+    m, D = branch.shape
+    if tuple(stream_in.shape) != (m, D) or not stream_in.is_contiguous() or not stream_in.is_cuda:
+        raise ValueError("stream_in must be a contiguous device tensor shaped like the branch")
+    if stream_in.dtype == torch.float32:
+        sk = 0
+    elif stream_in.dtype == torch.bfloat16:
+        sk = 1
+    else:
+        raise ValueError("stream_in must be float32 or bf16")
+    for g, name in ((alpha, "alpha"), (beta, "beta")):
+        if g.dtype != torch.float32 or tuple(g.shape) != (D,) or not g.is_contiguous() or not g.is_cuda:
+            raise ValueError(f"{name} must be a contiguous float32 device tensor [8192]")
+    pk = _boundary_kind(post_w, "post_w")
+    qk = _boundary_kind(pre_w, "pre_w")
+    if out is None:
+        out = torch.empty((m, D), dtype=torch.bfloat16, device=branch.device)
+    if store_stream and stream_out is None:
+        stream_out = torch.empty((m, D), dtype=torch.float32, device=branch.device)
+    if not store_stream:
+        stream_out = None
+    flags = (1 if post_input_scale else 0) | (2 if pre_input_scale else 0)
+    _check(_load().nrc_draft_boundary(_ptr(branch), m, D, _ptr(stream_in), sk, _ptr(alpha), _ptr(beta),
+                                      _ptr(post_w), pk, _ptr(pre_w), qk, post_eps, pre_eps, post_center, pre_center,
+                                      flags, _ptr(stream_out), _ptr(out), _stream(stream)))
+    return stream_out, out
 
 
 def context_hidden_norm(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hidden_center=0.0, pre_center=0.0,

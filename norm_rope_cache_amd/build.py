@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnrc.so")
-SOURCES = ["api.cpp", "context_norms.hip", "norms_ex.hip", "kv_project.hip", "kv_store.hip", "selftest.hip"]
+SOURCES = ["api.cpp", "context_norms.hip", "norms_ex.hip", "draft_boundary.hip", "kv_project.hip", "kv_store.hip", "selftest.hip"]
 
 ARCH = "gfx950"
 COMMON = [

@@ -110,6 +110,37 @@ int32_t nrc_context_norms_ex(const uint16_t* x, int64_t T, int64_t D, const void
     return launch_status(nrc::launch_norms_ex(a, (hipStream_t)stream), "context_norms_ex");
 }
 
+int32_t nrc_draft_boundary(const uint16_t* branch, int64_t m, int64_t D, const void* stream_in, int32_t stream_kind,
+                           const float* alpha, const float* beta, const void* post_w, int32_t post_kind,
+                           const void* pre_w, int32_t pre_kind, float post_eps, float pre_eps, float post_center,
+                           float pre_center, uint32_t flags, float* stream_out, uint16_t* out, void* stream) {
+    if (D != NRC_HIDDEN) return fail(NRC_ENOTSUP, "draft_boundary: rows of %lld, not %d", (long long)D, NRC_HIDDEN);
+    if (m < 0) return fail(NRC_EINVAL, "draft_boundary: m = %lld < 0", (long long)m);
+    if (stream_kind != NRC_STREAM_F32 && stream_kind != NRC_STREAM_BF16)
+        return fail(NRC_EINVAL, "draft_boundary: stream kind %d (0 FP32, 1 bf16)", stream_kind);
+    if (post_kind < NRC_WEIGHT_NONE || post_kind > NRC_WEIGHT_F16 || pre_kind < NRC_WEIGHT_NONE ||
+        pre_kind > NRC_WEIGHT_F16)
+        return fail(NRC_EINVAL, "draft_boundary: weight kinds %d, %d (0 none, 1 bf16, 2 FP32, 3 FP16)", post_kind,
+                    pre_kind);
+    if ((post_kind == NRC_WEIGHT_NONE) != (post_w == nullptr) || (pre_kind == NRC_WEIGHT_NONE) != (pre_w == nullptr))
+        return fail(NRC_EINVAL, "draft_boundary: a weight pointer must be NULL exactly when its kind is none");
+    if (flags & ~(uint32_t)(NRC_POST_INPUT_SCALE | NRC_PRE_INPUT_SCALE))
+        return fail(NRC_EINVAL, "draft_boundary: unknown flags 0x%x", flags);
+    if (m > ((int64_t)1 << 40) / D) return fail(NRC_EINVAL, "draft_boundary: m too large");
+    if (m == 0) return NRC_OK;
+    if (!branch || !stream_in || !alpha || !beta || !out)
+        return fail(NRC_EINVAL, "draft_boundary: NULL branch, stream, alpha, beta or out");
+    if (!aligned(branch, 16) || !aligned(stream_in, 16) || !aligned(alpha, 16) || !aligned(beta, 16) ||
+        !aligned(out, 16) || (stream_out && !aligned(stream_out, 16)) || (post_w && !aligned(post_w, 16)) ||
+        (pre_w && !aligned(pre_w, 16)))
+        return fail(NRC_EINVAL, "draft_boundary: operands must be 16-byte aligned");
+    nrc::BoundaryArgs a{branch, m, stream_in, stream_kind == NRC_STREAM_BF16, alpha, beta, post_w, post_kind,
+                        pre_w, pre_kind, post_eps, pre_eps, post_center, pre_center,
+                        (flags & NRC_POST_INPUT_SCALE) != 0, (flags & NRC_PRE_INPUT_SCALE) != 0, stream_out, out,
+                        num_cus()};
+    return launch_status(nrc::launch_draft_boundary(a, (hipStream_t)stream), "draft_boundary");
+}
+
 int32_t nrc_context_hidden_norm(const uint16_t* x, int64_t T, int64_t D, const uint16_t* hidden_w,
                                 const uint16_t* pre_w, int32_t L, float hidden_eps, float pre_eps,
                                 float hidden_center, float pre_center, uint16_t* h, float* r, void* stream) {

@@ -64,6 +64,27 @@ struct NormsExArgs {
 
 int launch_norms_ex(const NormsExArgs& a, hipStream_t stream);
 
+// The residual boundary (draft_boundary.hip).
+struct BoundaryArgs {
+    const uint16_t* branch;  // [m, 8192] bf16
+    int64_t m;
+    const void* stream_in;   // [m, 8192] FP32, or bf16 when stream_bf16
+    bool stream_bf16;
+    const float* alpha;      // [8192]
+    const float* beta;       // [8192]
+    const void* post_w;      // [8192] of post_kind (0 none, 1 bf16, 2 FP32, 3 FP16)
+    int32_t post_kind;
+    const void* pre_w;
+    int32_t pre_kind;
+    float post_eps, pre_eps, post_center, pre_center;
+    bool post_input_scale, pre_input_scale;
+    float* stream_out;       // [m, 8192] FP32, or nullptr
+    uint16_t* out;           // [m, 8192] bf16
+    int num_cus;
+};
+
+int launch_draft_boundary(const BoundaryArgs& a, hipStream_t stream);
+
 int launch_context_norms(const NormsArgs& a, hipStream_t stream);
 // h_out [T, 8192] bf16 and r_out [T]: the pre-pass of the fused projection (a.out unused).
 int launch_hidden_norm(const NormsArgs& a, uint16_t* h_out, float* r_out, hipStream_t stream);

@@ -57,6 +57,12 @@ def lib():
             ctypes.POINTER(ctypes.c_void_p), _i64p, _i64, _i64, _i64, _i64, _i64, _f32]
         L.nrc_oracle_kv_project_nd.restype = _i32
         L.nrc_oracle_kv_project_nd.argtypes = [_u16p, _u16p, _f32p, _i32, _i64, _i64, _i64]
+        L.nrc_oracle_f16_to_f32.restype = _f32
+        L.nrc_oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.nrc_oracle_draft_boundary.restype = _i32
+        L.nrc_oracle_draft_boundary.argtypes = [
+            _u16p, _i64, ctypes.c_void_p, _i32, _f32p, _f32p, ctypes.c_void_p, _i32, ctypes.c_void_p, _i32,
+            _f32, _f32, _f32, _f32, _i32, _f32p, _u16p]
         L.nrc_oracle_hidden_norm.argtypes = [_u16p, _i64, _i64, _u16p, _f32, _f32, _f32, _u16p, _f32p]
         L.nrc_oracle_hidden_norm.restype = _i32
         L.nrc_oracle_kv_project.argtypes = [_u16p, _u16p, _f32p, _i32, _i64, _i64, _i64]
@@ -294,6 +300,52 @@ def context_kv_store_ex(kv, H, positions, slots, cos_sin, caches, block_size, nu
         _ptr(cs, ctypes.c_uint16), max_pos, cp, _ptr(clen, ctypes.c_int64), num_blocks, block_size, block_stride,
         page_stride, head_stride, eps)
     _check(st, "context_kv_store_ex")
+
+
+def f16_to_f32(h):
+    return np.float32(lib().nrc_oracle_f16_to_f32(int(h)))
+
+
+def _bweight(w, kind):
+    """(kind code, array) of a boundary norm weight: None; uint16 bf16 bits
+    (kind 'bf16') or f16 bits (kind 'f16'); float32."""
+    if w is None:
+        return 0, None
+    w = np.ascontiguousarray(w)
+    assert w.shape == (D,)
+    if w.dtype == np.float32:
+        return 2, w
+    assert w.dtype == np.uint16
+    return (3 if kind == "f16" else 1), w
+
+
+def draft_boundary(branch, stream, alpha, beta, post_w=None, pre_w=None, post_eps=1e-6, pre_eps=1e-6,
+                   post_center=0.0, pre_center=0.0, post_input_scale=False, pre_input_scale=False,
+                   post_kind="bf16", pre_kind="bf16", store_stream=True):
+    """The residual boundary. branch [m, 8192] bf16 bits; stream [m, 8192]
+    float32 or bf16 bits (uint16); alpha, beta float32 [8192]; weights None,
+    float32, or uint16 bits read as bf16 or f16 (post_kind / pre_kind).
+    Returns (new stream float32 or None, out bf16 bits)."""
+    branch = _c(branch, np.uint16)
+    m = branch.shape[0]
+    assert branch.shape == (m, D)
+    stream = np.ascontiguousarray(stream)
+    assert stream.shape == (m, D) and stream.dtype in (np.float32, np.uint16)
+    sk = 0 if stream.dtype == np.float32 else 1
+    alpha = _c(alpha, np.float32)
+    beta = _c(beta, np.float32)
+    pk, pw = _bweight(post_w, post_kind)
+    qk, qw = _bweight(pre_w, pre_kind)
+    out = np.empty((m, D), dtype=np.uint16)
+    new = np.empty((m, D), dtype=np.float32) if store_stream else None
+    flags = (1 if post_input_scale else 0) | (2 if pre_input_scale else 0)
+    st = lib().nrc_oracle_draft_boundary(
+        _ptr(branch, ctypes.c_uint16), m, stream.ctypes.data, sk, _ptr(alpha, ctypes.c_float),
+        _ptr(beta, ctypes.c_float), None if pw is None else pw.ctypes.data, pk,
+        None if qw is None else qw.ctypes.data, qk, post_eps, pre_eps, post_center, pre_center, flags,
+        _ptr(new, ctypes.c_float), _ptr(out, ctypes.c_uint16))
+    _check(st, "draft_boundary")
+    return new, out
 
 
 def chain(x, hidden_w, pre_w, L, w_kv, H, positions, slots, cos_sin, caches, block_size,

@@ -458,6 +458,94 @@ int nrc_oracle_context_kv_store_ex(const uint16_t *kv, int32_t L, int64_t T, int
     return status;
 }
 
+/* ------------------------------------------------- the residual boundary */
+
+/* Exact f16 -> f32 (every f16 is an f32): sign, then zero / subnormal
+ * (mantissa * 2^-24) / normal (rebias the exponent by 112) / Inf / NaN. */
+static float f_of_f16(uint16_t h) {
+    const uint32_t sign = (uint32_t)(h >> 15) << 31;
+    const uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
+    float v;
+    if (e == 0) {
+        v = (float)m * 0x1p-24f; /* exact: m < 2^10 */
+        uint32_t u;
+        memcpy(&u, &v, sizeof u);
+        u |= sign;
+        memcpy(&v, &u, sizeof v);
+        return v;
+    }
+    uint32_t u = sign | (e == 31 ? (0xFFu << 23) | (m << 13) : ((e + 112u) << 23) | (m << 13));
+    memcpy(&v, &u, sizeof v);
+    return v;
+}
+
+float nrc_oracle_f16_to_f32(uint16_t h) { return f_of_f16(h); }
+
+enum { W_F16 = 3 };
+
+static float boundary_gamma(const void *w, int kind, float center, int c) {
+    float v = kind == W_BF16 ? f_of(((const uint16_t *)w)[c])
+              : kind == W_F16 ? f_of_f16(((const uint16_t *)w)[c])
+                              : ((const float *)w)[c];
+    return v + center;
+}
+
+/* One residual boundary of the DSpark draft ([BND] module summary and
+ * boundary_fragments): per row of the bf16 branch x,
+ *   post norm: (input-scaled: u = gamma_post * x) S1 = sum of squares in the
+ *     library's order, r1 = rs(fma(S1, 1/8192, post_eps)), y = u * r1, then
+ *     * gamma_post when output-scaled;
+ *   residual: res = alpha * stream + beta * bf16(y), each product rounded,
+ *     then the sum (FP32); the new stream is res, z = bf16(res);
+ *   pre norm of z, the same form with gamma_pre, rounded to bf16 -> out.
+ * stream: FP32 (stream_kind 0) or bf16 bits (1), [m, 8192]; alpha, beta
+ * FP32 [8192]; post_w / pre_w [8192] of kind 0 (none), 1 (bf16), 2 (FP32) or
+ * 3 (FP16); flags bit 0: post input-scaled, bit 1: pre input-scaled;
+ * stream_out [m, 8192] FP32 or NULL. */
+int nrc_oracle_draft_boundary(const uint16_t *branch, int64_t m, const void *stream, int32_t stream_kind,
+                              const float *alpha, const float *beta, const void *post_w, int32_t post_kind,
+                              const void *pre_w, int32_t pre_kind, float post_eps, float pre_eps, float post_center,
+                              float pre_center, int32_t flags, float *stream_out, uint16_t *out) {
+    if (m < 0 || !branch || !stream || !alpha || !beta || !out || stream_kind < 0 || stream_kind > 1) return ORACLE_EINVAL;
+    if (post_kind < 0 || post_kind > 3 || pre_kind < 0 || pre_kind > 3) return ORACLE_EINVAL;
+    if ((post_kind == 0) != (post_w == NULL) || (pre_kind == 0) != (pre_w == NULL)) return ORACLE_EINVAL;
+    const int post_in = post_kind != 0 && (flags & 1), pre_in = pre_kind != 0 && (flags & 2);
+    float *u = malloc(sizeof(float) * ROW_D), *z = malloc(sizeof(float) * ROW_D);
+    if (!u || !z) {
+        free(u);
+        free(z);
+        return ORACLE_EINVAL;
+    }
+    for (int64_t t = 0; t < m; ++t) {
+        for (int c = 0; c < ROW_D; ++c) {
+            float x = f_of(branch[t * ROW_D + c]);
+            u[c] = post_in ? boundary_gamma(post_w, post_kind, post_center, c) * x : x;
+        }
+        const float r1 = rs(fmaf(sumsq_row(u), 0x1p-13f, post_eps));
+        for (int c = 0; c < ROW_D; ++c) {
+            float y = u[c] * r1;
+            if (post_kind != 0 && !post_in) y = y * boundary_gamma(post_w, post_kind, post_center, c);
+            const float s = stream_kind == 0 ? ((const float *)stream)[t * ROW_D + c]
+                                             : f_of(((const uint16_t *)stream)[t * ROW_D + c]);
+            const float a = alpha[c] * s;
+            const float b = beta[c] * f_of(bf(y));
+            const float res = a + b;
+            if (stream_out) stream_out[t * ROW_D + c] = res;
+            const float zc = f_of(bf(res));
+            z[c] = pre_in ? boundary_gamma(pre_w, pre_kind, pre_center, c) * zc : zc;
+        }
+        const float r2 = rs(fmaf(sumsq_row(z), 0x1p-13f, pre_eps));
+        for (int c = 0; c < ROW_D; ++c) {
+            float o = z[c] * r2;
+            if (pre_kind != 0 && !pre_in) o = o * boundary_gamma(pre_w, pre_kind, pre_center, c);
+            out[t * ROW_D + c] = bf(o);
+        }
+    }
+    free(u);
+    free(z);
+    return 0;
+}
+
 /* The whole chain: norms, projection (rounded to bf16), store. normed
  * [L, T, 8192] and kv [L, T, N] are caller-provided scratch that receive the
  * intermediate results. */

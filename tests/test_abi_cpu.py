@@ -120,6 +120,29 @@ def test_store_ex_argument_checks(lib):
     assert call(rows=(ctypes.c_int64 * 2)(0, 5), k=None, v=None) == 0
 
 
+def test_boundary_argument_checks(lib):
+    f = lib.nrc_draft_boundary
+    ok = dict(br=FAKE, m=4, D=8192, s=FAKE, sk=0, a=FAKE, b=FAKE, pw=None, pk=0, qw=None, qk=0, flags=0, so=None,
+              out=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["br"], a["m"], a["D"], a["s"], a["sk"], a["a"], a["b"], a["pw"], a["pk"], a["qw"], a["qk"],
+                 1e-6, 1e-6, 0.0, 0.0, a["flags"], a["so"], a["out"], None)
+
+    assert call(D=4096) == ENOTSUP
+    assert call(m=-1) == EINVAL
+    assert call(sk=2) == EINVAL
+    assert call(pk=4, pw=FAKE) == EINVAL
+    assert call(pk=3) == EINVAL            # FP16 kind without a pointer
+    assert call(qw=FAKE) == EINVAL         # pointer with kind none
+    assert call(flags=4) == EINVAL
+    assert call(a=None) == EINVAL
+    assert call(so=MISALIGNED) == EINVAL
+    assert call(s=MISALIGNED) == EINVAL
+    assert call(m=0, br=None, s=None, a=None, b=None, out=None) == 0
+
+
 def test_project_argument_checks(lib):
     f = lib.nrc_context_kv_project
     assert f(FAKE, FAKE, FAKE, 0, 8, 8192, 1024, None) == EINVAL

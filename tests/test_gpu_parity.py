@@ -236,6 +236,98 @@ def test_norms_ex_plain_form_is_the_norms(nrc):
     assert_bits_equal(b, a, "norms_ex plain form")
 
 
+# ------------------------------------------------------ the residual boundary
+
+def _bw(kind, seed):
+    from norm_rope_cache_amd import synth
+
+    if kind is None:
+        return None, "bf16"
+    w = synth.normal_f32(seed, (8192,), 1.0, 0.4)
+    if kind == "bf16":
+        return synth.to_bf16_bits(w), "bf16"
+    if kind == "f16":
+        return w.astype(np.float16).view(np.uint16), "f16"
+    return w, "f32"
+
+
+def _bw_dev(w, kind):
+    import torch
+
+    if w is None:
+        return None
+    if kind == "f16":
+        return torch.from_numpy(w.view(np.float16)).cuda()
+    return to_dev(w)
+
+
+@pytest.mark.parametrize("pk", [None, "bf16", "f16", "f32"])
+@pytest.mark.parametrize("qk", [None, "bf16", "f16", "f32"])
+def test_boundary_parity(nrc, oracle, pk, qk):
+    """Every weight kind of each norm, both scalings, FP32 and bf16 streams,
+    with and without the stored stream, non-zero centers: the bf16 output and
+    the FP32 new stream bit-exact against the oracle."""
+    from norm_rope_cache_amd import synth
+
+    m = 37
+    x = synth.normal_bf16(9501, (m, 8192), 0.0, 1.5)
+    x[4] = 0
+    s32 = synth.normal_f32(9502, (m, 8192), 0.0, 2.0)
+    alpha = synth.normal_f32(9503, (8192,), 1.0, 0.2)
+    beta = synth.normal_f32(9504, (8192,), 0.5, 0.2)
+    pw, pks = _bw(pk, 9505)
+    qw, qks = _bw(qk, 9506)
+    for stream_bf16 in (False, True):
+        sin = synth.to_bf16_bits(s32) if stream_bf16 else s32
+        for pin, qin in ((False, False), (True, True), (False, True)):
+            for store in (True, False):
+                _say(f"boundary pk={pk} qk={qk} bf16 stream={stream_bf16} in={pin},{qin} store={store}")
+                new_d, out_d = nrc.draft_boundary(to_dev(x), to_dev(sin), to_dev(alpha), to_dev(beta),
+                                                  _bw_dev(pw, pks), _bw_dev(qw, qks), 1e-6, 2e-6, 0.125, -0.25,
+                                                  pin, qin, store_stream=store)
+                new, out = oracle.draft_boundary(x, sin, alpha, beta, pw, qw, 1e-6, 2e-6, 0.125, -0.25, pin, qin,
+                                                 pks, qks, store)
+                assert_bits_equal(to_host(out_d), out, f"boundary out {pk} {qk} {stream_bf16} {pin} {qin}")
+                if store:
+                    assert_bits_equal(to_host(new_d).view(np.uint32), new.view(np.uint32),
+                                      f"boundary stream {pk} {qk} {stream_bf16} {pin} {qin}")
+                else:
+                    assert new_d is None
+
+
+def test_boundary_special_values_and_grid_stride(nrc, oracle):
+    """NaN / Inf / subnormal / near-max branch and stream values, zero and
+    -0 gates and weights, eps = 0, and more rows than workgroups."""
+    from norm_rope_cache_amd import synth
+
+    m = 2300
+    x = synth.normal_bf16(9601, (m, 8192))
+    x[:64] = synth.edge_mixture_bf16(9602, 9603, (64, 8192), nan_inf=True)
+    x[64] = 0x8000
+    s = synth.normal_f32(9604, (m, 8192), 0.0, 3.0)
+    s[70, ::5] = np.inf
+    s[71, ::7] = np.nan
+    s[72] = 3e38
+    alpha = synth.normal_f32(9605, (8192,), 1.0, 0.2)
+    beta = synth.normal_f32(9606, (8192,), 1.0, 0.2)
+    alpha[::97] = 0.0
+    beta[::89] = -0.0
+    pw = synth.normal_f32(9607, (8192,), 1.0, 0.5)
+    pw[::101] = -0.0
+    qw = synth.to_bf16_bits(synth.normal_f32(9608, (8192,), 1.0, 0.5))
+    rows = np.unique(np.concatenate([np.arange(80), np.arange(80, m, 41), [m - 1]]))
+    for pe, qe in ((1e-6, 1e-6), (0.0, 0.0)):
+        _say(f"boundary specials eps={pe},{qe}")
+        new_d, out_d = nrc.draft_boundary(to_dev(x), to_dev(s), to_dev(alpha), to_dev(beta), to_dev(pw), to_dev(qw),
+                                          pe, qe)
+        new, out = oracle.draft_boundary(np.ascontiguousarray(x[rows]), np.ascontiguousarray(s[rows]), alpha, beta,
+                                         pw, qw, pe, qe)
+        assert_bits_equal(to_host(out_d)[rows], out, f"boundary specials out {pe}")
+        nd = to_host(new_d)[rows]
+        same = (nd.view(np.uint32) == new.view(np.uint32)) | (np.isnan(nd) & np.isnan(new))
+        assert same.all(), f"boundary specials stream {pe}: {int((~same).sum())} differ"
+
+
 # ---------------------------------------------------------------- projection
 
 def _project_check(nrc, oracle, A, B, rows=None, what=""):

@@ -566,6 +566,112 @@ def test_norms_ex_large_eps_closed_form(oracle):
         assert (a != b).mean() > 0.05
 
 
+# ------------------------------------------------------ the residual boundary
+
+def test_f16_to_f32_exhaustive(oracle):
+    """Every f16 bit pattern converts as numpy's float16 -> float32 (a NaN
+    stays a NaN)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    want = bits.view(np.float16).astype(np.float32)
+    got = np.array([oracle.f16_to_f32(b) for b in bits], dtype=np.float32)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
+def _boundary_case(rng, m, small):
+    x = rng.standard_normal((m, D)) * (0.08 if small else 1.0)
+    if small:
+        x = np.clip(x, -0.25, 0.25)
+    x = bf16_bits_of(x)
+    x[x == 0] = 0x3F80
+    x[x == 0x8000] = 0x3F80
+    s = (rng.standard_normal((m, D)) * (0.05 if small else 1.0)).astype(np.float32)
+    alpha = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    beta = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    return x, s, alpha, beta
+
+
+def _weights(rng, kind):
+    w = (1.0 + 0.3 * rng.standard_normal(D)).astype(np.float32)
+    if kind == "bf16":
+        return bf16_bits_of(w), f32_of_bf16(bf16_bits_of(w))
+    if kind == "f16":
+        h = w.astype(np.float16)
+        return h.view(np.uint16), h.astype(np.float32)
+    if kind == "f32":
+        return w, w
+    return None, None
+
+
+def test_boundary_with_zero_alpha_is_the_two_norms(oracle):
+    """Page '...draft_boundary' (module summary): with alpha = 0 and beta = 1
+    the residual is the post norm's bf16 output itself (0 * stream adds a
+    zero), so the boundary's output is pre_norm(bf16(post_norm(x))), which
+    is the (pinned) context norms with one layer: post -> hidden norm, pre ->
+    layer norm. FP16 weights read exactly equal their FP32 values."""
+    rng = np.random.default_rng(61)
+    m = 3
+    x, s, _, _ = _boundary_case(rng, m, False)
+    alpha = np.zeros(D, dtype=np.float32)
+    beta = np.ones(D, dtype=np.float32)
+    for pk in ("bf16", "f16", "f32", None):
+        for qk in ("bf16", "f16", "f32", None):
+            pw, pv = _weights(rng, pk)
+            qw, qv = _weights(rng, qk)
+            for pin, qin in ((False, False), (True, True), (True, False)):
+                _, out = oracle.draft_boundary(x, s, alpha, beta, pw, qw, 1e-6, 2e-6, 0.125, -0.25, pin, qin,
+                                               pk or "bf16", qk or "bf16")
+                hw = None if pk is None else (pw if pk in ("bf16", "f32") else pv)
+                lw = None if qk is None else (qw if qk in ("bf16", "f32") else qv)[None, :]
+                want = oracle.context_norms_ex(x, hw, lw, 1, 1e-6, 2e-6, 0.125, -0.25, pin, qin)[0]
+                assert np.array_equal(out, want), (pk, qk, pin, qin)
+
+
+def test_boundary_large_eps_closed_form(oracle):
+    """With both eps = 2^20 and small rows, both scales are exactly 2^-10, so
+    the boundary is a short chain of rounded FP32 operations: y = (x 2^-10)
+    gamma (input-scaled: (gamma x) 2^-10), res = alpha s + beta bf16(y) with
+    each product rounded, z = bf16(res), out = bf16((z 2^-10) gamma') (or
+    (gamma' z) 2^-10); the new stream is res. Expected values from numpy's
+    IEEE float32 ops and a midpoint-rule bf16 rounding, for every weight
+    kind, both scalings, FP32 and bf16 streams and non-zero centers."""
+    rng = np.random.default_rng(62)
+    m = 2
+    eps = np.float32(2.0 ** 20)
+    r = np.float32(2.0 ** -10)
+    pc, qc = np.float32(0.0625), np.float32(-0.125)
+    for pk in ("bf16", "f16", "f32", None):
+        for qk in ("bf16", "f16", "f32", None):
+            x, s, alpha, beta = _boundary_case(rng, m, True)
+            pw, pv = _weights(rng, pk)
+            qw, qv = _weights(rng, qk)
+            for stream_bf16 in (False, True):
+                sin = bf16_bits_of(s) if stream_bf16 else s
+                sv = f32_of_bf16(sin) if stream_bf16 else s
+                for pin in (False, True):
+                    for qin in (False, True):
+                        new, out = oracle.draft_boundary(x, sin, alpha, beta, pw, qw, float(eps), float(eps),
+                                                         float(pc), float(qc), pin, qin, pk or "bf16", qk or "bf16")
+                        xf = f32_of_bf16(x)
+                        if pv is None:
+                            y = xf * r
+                        elif pin:
+                            y = ((pv + pc) * xf) * r
+                        else:
+                            y = (xf * r) * (pv + pc)
+                        res = alpha * sv + beta * f32_of_bf16(_bf16_round_indep(y))
+                        assert np.array_equal(new.view(np.uint32), res.view(np.uint32)), (pk, qk, pin, qin)
+                        z = f32_of_bf16(_bf16_round_indep(res))
+                        if qv is None:
+                            o = z * r
+                        elif qin:
+                            o = ((qv + qc) * z) * r
+                        else:
+                            o = (z * r) * (qv + qc)
+                        assert np.array_equal(out, _bf16_round_indep(o)), (pk, qk, pin, qin, stream_bf16)
+
+
 # ------------------------------------------------------------ K-norm + RoPE
 
 def test_head_sumsq_order_golden(oracle):
