@@ -114,7 +114,15 @@ __global__ __launch_bounds__(kThreads) void draft_boundary_kernel(
     }
     for (int64_t row = blockIdx.x; row < m; row += gridDim.x) {
         const int64_t base = row * kHidden + col0;
-        float u[kFrags][8];
+        float u[kFrags][8], s[kFrags][8];
+        // the stream's loads go out with the branch's, before the first row sum
+#pragma unroll
+        for (int k = 0; k < kFrags; ++k) {
+            if constexpr (STREAM_BF16)
+                load_bf16x8(static_cast<const uint16_t*>(stream_in) + base + k * kChunk, s[k]);
+            else
+                load_f32x8(static_cast<const float*>(stream_in) + base + k * kChunk, s[k]);
+        }
 #pragma unroll
         for (int k = 0; k < kFrags; ++k) {
             load_bf16x8(branch + base + k * kChunk, u[k]);
@@ -126,17 +134,12 @@ __global__ __launch_bounds__(kThreads) void draft_boundary_kernel(
         const float r1 = rsqrt_rn(__builtin_fmaf(row_sum(lane_sumsq(u)), 0x1p-13f, post_eps));
 #pragma unroll
         for (int k = 0; k < kFrags; ++k) {
-            float s[8];
-            if constexpr (STREAM_BF16)
-                load_bf16x8(static_cast<const uint16_t*>(stream_in) + base + k * kChunk, s);
-            else
-                load_f32x8(static_cast<const float*>(stream_in) + base + k * kChunk, s);
             float res[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 float y = u[k][i] * r1;
                 if (post_w_on && !post_in) y = y * gp[k][i];
-                const float a = al[k][i] * s[i];
+                const float a = al[k][i] * s[k][i];
                 const float b = be[k][i] * bf16_lo(to_bf16(y));
                 res[i] = a + b;
                 float z = bf16_lo(to_bf16(res[i]));
