@@ -835,7 +835,8 @@ def test_insert_strided_views_and_slot_groups_brute_force(oracle):
     kv = bf16_bits_of(rng.standard_normal((L, T, N)) * 1.8)
     pos = rng.integers(0, 64, T).astype(np.int64)
     tab = bf16_bits_of(rng.uniform(-1, 1, (64, 64)))
-    slots = [rng.permutation(nb * bs)[:10].astype(np.int64), None, rng.permutation(nb * bs)[:7].astype(np.int64)]
+    # lists of their own lengths: the first layer's is the shortest
+    slots = [rng.permutation(nb * bs)[:6].astype(np.int64), None, rng.permutation(nb * bs)[:11].astype(np.int64)]
     slots[0][3] = -1
     slots[2][0] = -5
     layouts = {
