@@ -328,6 +328,48 @@ def test_boundary_special_values_and_grid_stride(nrc, oracle):
         assert same.all(), f"boundary specials stream {pe}: {int((~same).sum())} differ"
 
 
+def test_new_entry_points_edge_cases(nrc, oracle):
+    """One row, twelve layers (norm variants), a single boundary row with a
+    bf16 stream and FP16 weights, and a store with a non-power-of-two block
+    size through strided views: bit-exact against the oracle."""
+    import torch
+    from norm_rope_cache_amd import synth
+
+    x = synth.normal_bf16(9701, (1, 8192))
+    pw = synth.normal_f32(9702, (12, 8192), 1.0, 0.3)
+    got = nrc.context_norms_ex(to_dev(x), None, to_dev(pw), 12, 1e-6, 1e-6, 0.0, 0.5, False, True)
+    want = oracle.context_norms_ex(x, None, pw, 12, 1e-6, 1e-6, 0.0, 0.5, False, True)
+    assert_bits_equal(to_host(got), want, "norms_ex one row, 12 layers")
+
+    s = synth.to_bf16_bits(synth.normal_f32(9703, (1, 8192)))
+    a = synth.normal_f32(9704, (8192,), 1.0, 0.1)
+    b = synth.normal_f32(9705, (8192,), 1.0, 0.1)
+    w16 = synth.normal_f32(9706, (8192,), 1.0, 0.3).astype(np.float16)
+    new_d, out_d = nrc.draft_boundary(to_dev(x), to_dev(s), to_dev(a), to_dev(b), torch.from_numpy(w16).cuda(),
+                                      torch.from_numpy(w16).cuda(), 1e-5, 1e-5, 0.0, 0.0, True, False)
+    new, out = oracle.draft_boundary(x, s, a, b, w16.view(np.uint16), w16.view(np.uint16), 1e-5, 1e-5, 0.0, 0.0,
+                                     True, False, "f16", "f16")
+    assert_bits_equal(to_host(out_d), out, "boundary one row")
+    assert_bits_equal(to_host(new_d).view(np.uint32), new.view(np.uint32), "boundary one row stream")
+
+    L, T, H, bs, nb = 2, 9, 2, 7, 11
+    kv = synth.normal_bf16(9707, (L, T, 2 * H * 64))
+    pos = np.arange(T, dtype=np.int64)
+    tab = synth.to_bf16_bits(np.random.default_rng(5).uniform(-1, 1, (T, 64)))
+    slots = [np.random.default_rng(6).permutation(nb * bs)[:T].astype(np.int64), np.array([3, -1, 76], np.int64)]
+    bstr, pstr, hstr = H * bs * 136, 136, bs * 136
+    size = (nb - 1) * bstr + (bs - 1) * pstr + (H - 1) * hstr + 128
+    prior = [synth.random_bits_u16(9710 + l, (size,)) for l in range(L)]
+    want = [p.copy() for p in prior]
+    oracle.context_kv_store_ex(kv, H, pos, slots, tab, want, bs, nb, bstr, pstr, hstr, 1e-6)
+    flats = [to_dev(p) for p in prior]
+    views = [torch.as_strided(f, (nb, H, bs, 128), (bstr, hstr, pstr, 1)) for f in flats]
+    nrc.context_kv_store_ex(to_dev(kv), to_dev(pos), [to_dev(sl) for sl in slots], to_dev(tab), views, H, 1e-6)
+    torch.cuda.synchronize()
+    for l in range(L):
+        assert_bits_equal(to_host(flats[l]), want[l], f"store_ex block size 7 layer {l}")
+
+
 # ---------------------------------------------------------------- projection
 
 def _project_check(nrc, oracle, A, B, rows=None, what=""):
