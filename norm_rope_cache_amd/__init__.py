@@ -7,11 +7,14 @@ runs in the library's HIP kernels; there is no CPU or PyTorch fallback: if
 libnrc.so is missing, every call raises.
 
     context_norms(x, hidden_w, pre_w, L, ...)      -> [L, T, 8192] bf16
-    context_kv_project(normed, w_kv)               -> [L, T, N] bf16
+    context_norms_ex(...)                          the same with FP32 / input-scaled weights
+    context_kv_project(normed, w_kv)               -> [L, T, N] bf16 ([L, D, N] or [L, N, D] weights)
     context_kv_store(kv, positions, slots, cos_sin, caches, H, ...)   (in place)
+    context_kv_store_ex(...)                       per-layer slot lists, strided cache views
     context_hidden_norm(x, ...) -> (h, r)          pre-pass of the fused path
     context_kv_project_fused(h, r, pre_w, w_kv)    projection with the layer norms fused in
-    context_kv_chain(...)                          the whole chain (fused by default)
+    context_kv_chain(...)                          the whole chain (unfused by default)
+    draft_boundary(branch, stream_in, alpha, beta, ...)   the residual boundary
 """
 
 import ctypes
@@ -20,8 +23,11 @@ import os
 __all__ = [
     "NrcError",
     "context_norms",
+    "context_norms_ex",
     "context_kv_project",
     "context_kv_store",
+    "context_kv_store_ex",
+    "draft_boundary",
     "context_kv_chain",
     "context_hidden_norm",
     "context_kv_project_fused",
@@ -493,12 +499,14 @@ def check_bf16_pair(x, stream=None):
 
 
 def context_kv_chain(x, hidden_w, pre_w, w_kv, positions, slots, cos_sin, caches, H, hidden_eps=1e-6,
-                     pre_eps=1e-6, k_eps=1e-6, fused=True, workspace=None, kv=None, stream=None):
+                     pre_eps=1e-6, k_eps=1e-6, fused=False, workspace=None, kv=None, stream=None):
     """The whole chain, in place on `caches`; returns kv [L, T, N].
 
-    fused=True: pre-pass (h, r) -> fused projection -> store; `workspace` may
-    be a tuple (h [T, 8192] bf16, r [T] float32). fused=False: norms into
-    `workspace` ([L, T, 8192] bf16) -> projection -> store."""
+    fused=False (the faster form on MI355X): norms into `workspace`
+    ([L, T, 8192] bf16) -> projection -> store. fused=True: pre-pass (h, r)
+    -> fused projection -> store, without the [L, T, 8192] intermediate;
+    `workspace` may be a tuple (h [T, 8192] bf16, r [T] float32). Both write
+    the same bits."""
     L = w_kv.shape[0]
     if fused:
         h, r = workspace if workspace is not None else (None, None)

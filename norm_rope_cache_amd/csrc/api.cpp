@@ -13,6 +13,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <vector>
 
 #include "../../include/nrc.h"
@@ -32,16 +33,18 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// CUs of the current device, looked up once per device (relaxed atomics:
+// concurrent first calls store the same value).
 int num_cus() {
-    static int cache[64] = {};
+    static std::atomic<int> cache[64] = {};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    int n = dev < 64 ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev] = n;
+        if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 int launch_status(int rc, const char* what) {

@@ -316,20 +316,13 @@ void launch_w(const NormsArgs& a, dim3 grid, size_t lds, uint16_t* h_out, float*
 
 template <bool WEIGHTS_IN_LDS, bool ADD_CENTER, bool PREPASS>
 int set_lds_limit() {
-    // The opt-in above 64 KiB of LDS is per kernel and device.
-    static bool done[64][4] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+    static std::atomic<int> done[4][64] = {};
     const void* fns[4] = {(const void*)context_norms_kernel<WEIGHTS_IN_LDS, true, true, ADD_CENTER, PREPASS>,
                           (const void*)context_norms_kernel<WEIGHTS_IN_LDS, true, false, ADD_CENTER, PREPASS>,
                           (const void*)context_norms_kernel<WEIGHTS_IN_LDS, false, true, ADD_CENTER, PREPASS>,
                           (const void*)context_norms_kernel<WEIGHTS_IN_LDS, false, false, ADD_CENTER, PREPASS>};
-    for (int i = 0; i < 4; ++i) {
-        if (done[dev][i]) continue;
-        if (hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, 9 * kRowBytes) != hipSuccess)
-            return -1;
-        done[dev][i] = true;
-    }
+    for (int i = 0; i < 4; ++i)
+        if (raise_lds_limit(fns[i], 9 * kRowBytes, done[i])) return -1;
     return 0;
 }
 

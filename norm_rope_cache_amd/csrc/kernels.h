@@ -5,7 +5,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace nrc {
+
+// Raise a kernel's dynamic-LDS limit to `bytes` on the current device (the
+// opt-in above 64 KiB is per kernel and device). `done` caches per device
+// the largest limit set so far; setting it twice from racing threads is
+// harmless. Returns 0, or -1 when the runtime refuses.
+template <int DEVICES>
+inline int raise_lds_limit(const void* kernel, int bytes, std::atomic<int> (&done)[DEVICES]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    if (dev < DEVICES && done[dev].load(std::memory_order_relaxed) >= bytes) return 0;
+    if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess) return -1;
+    if (dev < DEVICES) done[dev].store(bytes, std::memory_order_relaxed);
+    return 0;
+}
 
 constexpr int kMaxLayersPerLaunch = 8;
 

@@ -509,17 +509,8 @@ int launch_tiles(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
     const size_t lds_bytes = CF::LDS_BYTES + ((FUSED && PW) ? (size_t)a.K * 2 : 0);
     auto kernel = kv_project_kernel<BM, BN, WM, WN, FUSED, PW, CMODE, B_ND>;
     if (lds_bytes > 65536) {
-        // The opt-in above 64 KiB is per kernel and device; set it on each device once.
-        static int attr_set[64] = {};
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return -1;
-        if (dev < 0 || dev >= 64) return -1;
-        if (attr_set[dev] < (int)lds_bytes) {
-            if (hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
-                hipSuccess)
-                return -1;
-            attr_set[dev] = (int)lds_bytes;
-        }
+        static std::atomic<int> done[64] = {};
+        if (raise_lds_limit((const void*)kernel, (int)lds_bytes, done)) return -1;
     }
     // One persistent workgroup per LDS-resident slot (the ring and weights
     // take most of a CU's 160 KiB), never more than there are tiles.

@@ -724,7 +724,8 @@ def test_chain_parity(nrc, oracle, name, T, fused):
         f"chain cache values: max error {err.max()}"
 
 
-def test_deterministic(nrc):
+@pytest.mark.parametrize("fused", [False, True])
+def test_deterministic(nrc, fused):
     """Two runs of the chain give identical bits."""
     from norm_rope_cache_amd import synth
 
@@ -734,7 +735,8 @@ def test_deterministic(nrc):
     for _ in range(2):
         cd = to_dev(d["caches"])
         kv = nrc.context_kv_chain(to_dev(d["x"]), to_dev(d["hidden_w"]), to_dev(d["pre_w"]), to_dev(d["w_kv"]),
-                                  to_dev(d["positions"]), to_dev(d["slots"]), to_dev(d["cos_sin"]), cd, cfg.H)
+                                  to_dev(d["positions"]), to_dev(d["slots"]), to_dev(d["cos_sin"]), cd, cfg.H,
+                                  fused=fused)
         outs.append((to_host(kv), to_host(cd)))
     for a, b in zip(outs[0], outs[1]):
         assert np.array_equal(a, b)
