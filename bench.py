@@ -226,7 +226,20 @@ def main():
     rows_per_s = cfg.T * args.steps / wall
 
     # Norm variants (FP32 weights, weights scaling the norms' inputs), timed
-    # after the chain on the same rows: not part of the step.
+    # after the chain on the same rows: not part of the step. Each gets 20
+    # warm-up launches (a new kernel path runs slower for its first dozen or
+    # so launches on this GPU), then 20 timed back to back.
+    def time_launches(run, warmup=20, timed=20):
+        for _ in range(warmup):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(timed):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / timed
+
     variants = {}
     if not args.no_variants and hw is not None and pw is not None:
         hw32, pw32 = hw.float().contiguous(), pw.float().contiguous()
@@ -235,15 +248,7 @@ def main():
         for his, pis in ((False, False), (True, True)):
             run = lambda: nrc.context_norms_ex(x, hw32, pw32, cfg.L, d["hidden_eps"], d["pre_eps"],
                                                hidden_input_scale=his, pre_input_scale=pis, out=vout)
-            for _ in range(3):
-                run()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(10):
-                run()
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / 10
+            ms = time_launches(run)
             name = "context_norms_ex[fp32 weights" + (", input-scaled]" if his else "]")
             variants[name] = {"bound": "hbm", "ms": ms, "bytes": vb, "achieved_GBs": vb / (ms * 1e-3) / 1e9,
                               "frac": vb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
@@ -255,15 +260,7 @@ def main():
         s_out = torch.empty_like(s_in)
         b_out = torch.empty((cfg.T, 8192), dtype=torch.bfloat16, device=dev)
         run = lambda: nrc.draft_boundary(x, s_in, alpha, beta, hw, pw[0], out=b_out, stream_out=s_out)
-        for _ in range(3):
-            run()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(10):
-            run()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 10
+        ms = time_launches(run)
         bb = cfg.T * 8192 * (2 + 4 + 4 + 2) + 8192 * (4 + 4 + 2 + 2)
         variants["draft_boundary[fp32 stream in/out]"] = {"bound": "hbm", "ms": ms, "bytes": bb,
                                                          "achieved_GBs": bb / (ms * 1e-3) / 1e9,

@@ -91,6 +91,15 @@ __device__ __forceinline__ float lane_sumsq(const float (&u)[kFrags][8]) {
 
 __device__ __forceinline__ bool finite(float v) { return __builtin_fabsf(v) < __builtin_huge_valf(); }
 
+// Every gain w + center (FP32 add) of the eight bf16 weights is finite.
+__device__ __forceinline__ bool gains_finite8(const U32x4& w, float center) {
+    const uint32_t p[4] = {w.x, w.y, w.z, w.w};
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ok = ok && finite(bf16_lo(p[i]) + center) && finite(bf16_hi(p[i]) + center);
+    return ok;
+}
+
 constexpr int kSlots = 4;                  // rows in flight per workgroup (one per 256 threads)
 constexpr int kBlockThreads = kSlots * kThreads;
 constexpr int kRowBytes = kHidden * 2;     // 16 KiB of bf16 weights per norm
@@ -130,7 +139,8 @@ __global__ __launch_bounds__(kBlockThreads) void context_norms_kernel(
     const bool fix_p = !ADD_CENTER && !__builtin_signbit(pre_center);
 
     // ---- stage the weights (16-byte chunks, every thread a share) and check
-    // that all are finite (the fast bf16 conversion relies on it).
+    // that every gain is finite (the fast bf16 conversion relies on it; with
+    // a center the check is on w + center, which can overflow).
     bool wfinite = true;
     U32x4* wl = reinterpret_cast<U32x4*>(smem);
     const int hw_chunks = HW ? kRowBytes / 16 : 0;
@@ -144,16 +154,15 @@ __global__ __launch_bounds__(kBlockThreads) void context_norms_kernel(
             w = load16(pre_w + 8 * (c - hw_chunks));
             if (fix_p) w = plus_zero(w);
         }
-        wfinite = wfinite && finite8(w);
+        wfinite = wfinite && (ADD_CENTER ? gains_finite8(w, c < hw_chunks ? hidden_center : pre_center) : finite8(w));
         wl[c] = w;
     }
-    bool pfinite = true;  // layer weights (and center) finite
+    bool pfinite = true;  // layer gains finite
     if constexpr (PW && !WEIGHTS_IN_LDS) {
-        for (int c = tid; c < L * (kRowBytes / 16); c += kBlockThreads) pfinite = pfinite && finite8(load16(pre_w + 8 * c));
-    }
-    if constexpr (ADD_CENTER) {
-        wfinite = wfinite && finite(hidden_center);
-        pfinite = pfinite && finite(pre_center);
+        for (int c = tid; c < L * (kRowBytes / 16); c += kBlockThreads) {
+            const U32x4 w = load16(pre_w + 8 * c);
+            pfinite = pfinite && (ADD_CENTER ? gains_finite8(w, pre_center) : finite8(w));
+        }
     }
     if constexpr (PREPASS) {
         // the hidden conversion needs only the hidden weights finite

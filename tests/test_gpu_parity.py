@@ -222,6 +222,63 @@ def test_norms_ex_special_values_and_grid_stride(nrc, oracle):
         assert_bits_equal(got[:, rows], want, f"norms_ex specials {he},{pe},{his},{pis}")
 
 
+@pytest.mark.parametrize("kind,L", [("bf16", 4), ("bf16", 6), ("bf16", 8), ("f32", 4), ("f32", 5)])
+def test_norms_ex_layer_counts(nrc, oracle, kind, L):
+    """Layer weights staged as FP32 gains (up to 4 layers), as stored bf16 (5
+    to 8) and read from memory per row (FP32 beyond 4): bit-exact, both
+    scalings, on a row count that is not a multiple of the workgroup's."""
+    from norm_rope_cache_amd import synth
+
+    T = 19
+    x = synth.normal_bf16(9301, (T, 8192), 0.0, 1.5)
+    hw = _variant_weights(kind, (8192,), 9302)
+    pw = _variant_weights(kind, (L, 8192), 9303)
+    for his, pis in ((False, False), (True, True), (False, True)):
+        _say(f"norms_ex layers kind={kind} L={L} in={his},{pis}")
+        got = nrc.context_norms_ex(to_dev(x), to_dev(hw), to_dev(pw), L, 1e-6, 2e-6, 0.125, -0.25, his, pis)
+        want = oracle.context_norms_ex(x, hw, pw, L, 1e-6, 2e-6, 0.125, -0.25, his, pis)
+        assert_bits_equal(to_host(got), want, f"norms_ex layers {kind} {L} {his} {pis}")
+
+
+def test_norm_gains_overflowing_to_infinity(nrc, oracle):
+    """Finite weights whose gain w + center overflows to infinity: zeros of
+    the row then give 0 * inf = NaN, which must come out as 0x7FC0 (the
+    kernels' hardware conversion is only for rows whose gains are all
+    finite). Layer gains overflow under a finite hidden norm; the hidden
+    stage is checked on its own output (the fused form's pre-pass)."""
+    from norm_rope_cache_amd import synth
+
+    T, L = 9, 2
+    x = synth.normal_bf16(9401, (T, 8192), 0.0, 1.0)
+    x[:, ::7] = 0
+    x[2] = 0
+    hw = synth.normal_bf16(9402, (8192,), 1.0, 0.5)
+    pw = synth.normal_bf16(9403, (L, 8192), 1.0, 0.5)
+    pw[1, ::11] = 0x7F7F  # 3.39e38 + 1e38 = inf in FP32
+    for hc in (0.0, 0.5):
+        _say(f"norms overflowing layer gains hidden center={hc}")
+        got = nrc.context_norms(to_dev(x), to_dev(hw), to_dev(pw), L, 1e-6, 1e-6, hc, 1e38)
+        want = oracle.context_norms(x, hw, pw, L, 1e-6, 1e-6, hc, 1e38)
+        assert (want == 0x7FC0).any() and ((want & 0x7FFF) == 0x7F80).any()
+        assert_bits_equal(to_host(got), want, f"norms overflowing layer gains {hc}")
+    hbig = hw.copy()
+    hbig[::13] = 0x7F7F
+    _say("hidden norm overflowing gains")
+    h, _ = nrc.context_hidden_norm(to_dev(x), to_dev(hbig), None, L, 1e-6, 1e-6, 1e38, 0.0)
+    want_h, _ = oracle.hidden_norm(x, hbig, 1e-6, 1e38, 1e-6)
+    assert (want_h == 0x7FC0).any()
+    assert_bits_equal(to_host(h), want_h, "hidden norm overflowing gains")
+    hf = synth.normal_f32(9404, (8192,), 1.0, 0.5)
+    pf = synth.normal_f32(9405, (L, 8192), 1.0, 0.5)
+    pf[0, ::17] = 3e38
+    for hwk, pwk in ((hf, pf), (hw, pw), (hf, pw)):
+        for his, pis in ((False, False), (True, True), (True, False)):
+            _say(f"norms_ex overflowing layer gains {hwk.dtype},{pwk.dtype} in={his},{pis}")
+            got = nrc.context_norms_ex(to_dev(x), to_dev(hwk), to_dev(pwk), L, 1e-6, 1e-6, 0.0, 1e38, his, pis)
+            want = oracle.context_norms_ex(x, hwk, pwk, L, 1e-6, 1e-6, 0.0, 1e38, his, pis)
+            assert_bits_equal(to_host(got), want, f"norms_ex overflowing gains {hwk.dtype} {pwk.dtype} {his} {pis}")
+
+
 def test_norms_ex_plain_form_is_the_norms(nrc):
     """bf16 weights on the outputs through the general entry: the same bits as
     context_norms (it takes the same kernel)."""
