@@ -228,27 +228,35 @@ def main():
     # Norm variants (FP32 weights, weights scaling the norms' inputs), timed
     # after the chain on the same rows: not part of the step. Each gets 20
     # warm-up launches (a new kernel path runs slower for its first dozen or
-    # so launches on this GPU), then 20 timed back to back.
-    def time_launches(run, warmup=20, timed=20):
+    # so launches on this GPU), then 20 timed launches, each after an untimed
+    # read of 1 GiB of other memory: run back to back, the 256 MB infinity
+    # cache would keep most of the 268 MB input between launches (nontemporal
+    # outputs do not evict it), which the chain never sees.
+    def time_launches(run, flush_src, warmup=20, timed=20):
+        flush_dst = torch.empty(1, dtype=torch.float32, device=dev)
         for _ in range(warmup):
             run()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        total = 0.0
         for _ in range(timed):
+            torch.sum(flush_src, dim=0, out=flush_dst)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
             run()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / timed
+            e1.record()
+            torch.cuda.synchronize()
+            total += e0.elapsed_time(e1)
+        return total / timed
 
     variants = {}
     if not args.no_variants and hw is not None and pw is not None:
+        flush_src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
         hw32, pw32 = hw.float().contiguous(), pw.float().contiguous()
         vout = torch.empty((cfg.L, cfg.T, 8192), dtype=torch.bfloat16, device=dev)
         vb = cfg.T * (2 * 8192 + 2 * cfg.L * 8192) + 4 * 8192 * (1 + cfg.L)
         for his, pis in ((False, False), (True, True)):
             run = lambda: nrc.context_norms_ex(x, hw32, pw32, cfg.L, d["hidden_eps"], d["pre_eps"],
                                                hidden_input_scale=his, pre_input_scale=pis, out=vout)
-            ms = time_launches(run)
+            ms = time_launches(run, flush_src)
             name = "context_norms_ex[fp32 weights" + (", input-scaled]" if his else "]")
             variants[name] = {"bound": "hbm", "ms": ms, "bytes": vb, "achieved_GBs": vb / (ms * 1e-3) / 1e9,
                               "frac": vb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
@@ -260,12 +268,12 @@ def main():
         s_out = torch.empty_like(s_in)
         b_out = torch.empty((cfg.T, 8192), dtype=torch.bfloat16, device=dev)
         run = lambda: nrc.draft_boundary(x, s_in, alpha, beta, hw, pw[0], out=b_out, stream_out=s_out)
-        ms = time_launches(run)
+        ms = time_launches(run, flush_src)
         bb = cfg.T * 8192 * (2 + 4 + 4 + 2) + 8192 * (4 + 4 + 2 + 2)
         variants["draft_boundary[fp32 stream in/out]"] = {"bound": "hbm", "ms": ms, "bytes": bb,
                                                          "achieved_GBs": bb / (ms * 1e-3) / 1e9,
                                                          "frac": bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        del s_in, s_out, b_out
+        del s_in, s_out, b_out, flush_src
         log("variants: " + ", ".join(f"{k}={v['ms']:.4f} ms" for k, v in variants.items()))
 
     cpu = None
