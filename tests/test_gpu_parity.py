@@ -385,6 +385,43 @@ def test_boundary_special_values_and_grid_stride(nrc, oracle):
         assert same.all(), f"boundary specials stream {pe}: {int((~same).sum())} differ"
 
 
+def test_variants_full_size_as_benchmarked(nrc, oracle):
+    """The norm variants and the boundary on the long workload's 16384 rows,
+    in the forms bench.py times (FP32 weights with both scalings; FP32 stream
+    in and out with bf16 gains): bit-exact on a seeded sample of rows plus the
+    first and last (every launch covers all rows; the oracle computes the
+    sampled ones)."""
+    from norm_rope_cache_amd import synth
+
+    cfg = synth.CONFIGS["long"]
+    d = synth.make_inputs(cfg, with_cache=False)
+    T, L = cfg.T, cfg.L
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, T - 2, T - 1], rng.choice(T, 160, replace=False)]))
+    hw32 = f32(d["hidden_w"])
+    pw32 = f32(d["pre_w"])
+    x = to_dev(d["x"])
+    rows_d = torch.from_numpy(rows).cuda()
+    for his in (False, True):
+        _say(f"norms_ex full size input-scaled={his}")
+        got = to_host(nrc.context_norms_ex(x, to_dev(hw32), to_dev(pw32), L, d["hidden_eps"], d["pre_eps"],
+                                           hidden_input_scale=his, pre_input_scale=his)[:, rows_d])
+        want = oracle.context_norms_ex(np.ascontiguousarray(d["x"][rows]), hw32, pw32, L, d["hidden_eps"],
+                                       d["pre_eps"], 0.0, 0.0, his, his)
+        assert_bits_equal(got, want, f"norms_ex full size {his}")
+    _say("boundary full size")
+    s = synth.normal_f32(9701, (T, 8192), 0.0, 1.0)
+    alpha = np.full(8192, 0.9, dtype=np.float32)
+    beta = np.full(8192, 1.1, dtype=np.float32)
+    new_d, out_d = nrc.draft_boundary(x, to_dev(s), to_dev(alpha), to_dev(beta), to_dev(d["hidden_w"]),
+                                      to_dev(np.ascontiguousarray(d["pre_w"][0])))
+    new, out = oracle.draft_boundary(np.ascontiguousarray(d["x"][rows]), np.ascontiguousarray(s[rows]), alpha, beta,
+                                     d["hidden_w"], np.ascontiguousarray(d["pre_w"][0]))
+    assert_bits_equal(to_host(out_d[rows_d]), out, "boundary full size out")
+    nd = to_host(new_d[rows_d])
+    assert (nd.view(np.uint32) == new.view(np.uint32)).all(), "boundary full size stream"
+
+
 def test_new_entry_points_edge_cases(nrc, oracle):
     """One row, twelve layers (norm variants), a single boundary row with a
     bf16 stream and FP16 weights, and a store with a non-power-of-two block
