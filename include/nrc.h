@@ -174,6 +174,37 @@ int32_t nrc_context_kv_project_ex(const uint16_t* normed, const uint16_t* w, int
                                   int32_t L, int64_t T, int64_t D, int64_t N, void* stream);
 
 /*
+ * nrc_context_kv_project_workspace_bytes - bytes of workspace the split form
+ * of the projection needs for this shape on the current device, or 0 when
+ * the shape is not split. Shapes whose output tiles are too few to occupy
+ * the device's compute units split the D (summation) axis into 2, 4 or 8
+ * slices (the projection is a stock bmm, whose summation order is free).
+ * Page "...runtime.draft", ContextKV._project. Returns a negative status
+ * for shapes nrc_context_kv_project rejects.
+ */
+int64_t nrc_context_kv_project_workspace_bytes(int32_t L, int64_t T, int64_t D, int64_t N);
+
+/*
+ * nrc_context_kv_project_split - nrc_context_kv_project_ex that may split the
+ * summation axis for shapes with few output tiles (small T). Each slice's
+ * FP32 sums go to the workspace, then are added slice by slice in a fixed
+ * order (deterministic) and rounded to bf16 once. Page "...runtime.draft",
+ * ContextKV._project.
+ *
+ *   workspace        caller-owned device memory, 16-byte aligned, of at
+ *                    least nrc_context_kv_project_workspace_bytes(L, T, D, N)
+ *                    bytes; read and written by the call, contents on return
+ *                    unspecified. Unused (may be NULL) when that size is 0.
+ *   workspace_bytes  its size in bytes.
+ *   Other arguments as nrc_context_kv_project_ex. Errors as there, plus
+ *   NRC_EINVAL for a workspace that is NULL, too small or misaligned when
+ *   the shape splits. Calls that share a workspace must not overlap.
+ */
+int32_t nrc_context_kv_project_split(const uint16_t* normed, const uint16_t* w, int32_t w_layout, uint16_t* kv,
+                                     int32_t L, int64_t T, int64_t D, int64_t N, void* workspace,
+                                     int64_t workspace_bytes, void* stream);
+
+/*
  * nrc_context_hidden_norm - the pre-pass of the fused norms + projection: the
  * hidden norm and each row's layer-norm scale, the two quantities every
  * layer norm of a row shares. Page "...cutedsl.draft.context", ContextNorms

@@ -89,6 +89,10 @@ def _load():
                                      _f32, ctypes.c_uint32, _vp, _vp, _vp]
     L.nrc_context_kv_project.restype = _i32
     L.nrc_context_kv_project.argtypes = [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp]
+    L.nrc_context_kv_project_workspace_bytes.restype = _i64
+    L.nrc_context_kv_project_workspace_bytes.argtypes = [_i32, _i64, _i64, _i64]
+    L.nrc_context_kv_project_split.restype = _i32
+    L.nrc_context_kv_project_split.argtypes = [_vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp]
     L.nrc_context_kv_store.restype = _i32
     L.nrc_context_kv_store.argtypes = [
         _vp, _vp, _i64, _i64, _i64, _i64, _vp, ctypes.POINTER(_vp), _i64, _i64, _vp, _i64,
@@ -318,9 +322,12 @@ def context_kv_project_fused(h, r, pre_w, w_kv, pre_center=0.0, out=None, stream
     return out
 
 
-def context_kv_project(normed, w_kv, out=None, stream=None, w_layout="dn"):
+def context_kv_project(normed, w_kv, out=None, stream=None, w_layout="dn", split=True):
     """[L, T, D] x [L, D, N] -> [L, T, N] bf16 (FP32 accumulation).
-    w_layout "nd": w_kv is stored [L, N, D] (the pages' storage)."""
+    w_layout "nd": w_kv is stored [L, N, D] (the pages' storage). split: for
+    shapes with too few output tiles to fill the GPU (small T) the summation
+    axis is split over several workgroups, with a workspace from torch's
+    allocator (split=False keeps the one-pass kernel)."""
     import torch
 
     _bf16(normed, "normed")
@@ -342,11 +349,21 @@ def context_kv_project(normed, w_kv, out=None, stream=None, w_layout="dn"):
         _bf16(out, "out")
         if tuple(out.shape) != (L, T, N):
             raise ValueError("out must be [L, T, N]")
-    if w_layout == "dn":
-        _check(_load().nrc_context_kv_project(_ptr(normed), _ptr(w_kv), _ptr(out), L, T, D, N, _stream(stream)))
+    lib = _load()
+    layout = 0 if w_layout == "dn" else 1
+    need = lib.nrc_context_kv_project_workspace_bytes(L, T, D, N) if split else 0
+    if need < 0:
+        _check(need)
+    if need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=normed.device)
+        if stream is not None:
+            ws.record_stream(stream)  # the allocator may reuse it only after this stream's work
+        _check(lib.nrc_context_kv_project_split(_ptr(normed), _ptr(w_kv), layout, _ptr(out), L, T, D, N, _ptr(ws),
+                                                need, _stream(stream)))
+    elif w_layout == "dn":
+        _check(lib.nrc_context_kv_project(_ptr(normed), _ptr(w_kv), _ptr(out), L, T, D, N, _stream(stream)))
     else:
-        _check(_load().nrc_context_kv_project_ex(_ptr(normed), _ptr(w_kv), 1, _ptr(out), L, T, D, N,
-                                                 _stream(stream)))
+        _check(lib.nrc_context_kv_project_ex(_ptr(normed), _ptr(w_kv), 1, _ptr(out), L, T, D, N, _stream(stream)))
     return out
 
 
@@ -499,14 +516,16 @@ def check_bf16_pair(x, stream=None):
 
 
 def context_kv_chain(x, hidden_w, pre_w, w_kv, positions, slots, cos_sin, caches, H, hidden_eps=1e-6,
-                     pre_eps=1e-6, k_eps=1e-6, fused=False, workspace=None, kv=None, stream=None):
+                     pre_eps=1e-6, k_eps=1e-6, fused=False, workspace=None, kv=None, stream=None, split=True):
     """The whole chain, in place on `caches`; returns kv [L, T, N].
 
     fused=False (the faster form on MI355X): norms into `workspace`
     ([L, T, 8192] bf16) -> projection -> store. fused=True: pre-pass (h, r)
     -> fused projection -> store, without the [L, T, 8192] intermediate;
     `workspace` may be a tuple (h [T, 8192] bf16, r [T] float32). Both write
-    the same bits."""
+    the same bits when the unfused projection runs in one pass (split=False);
+    for small T it otherwise splits the summation (see context_kv_project),
+    which changes the rounding within the projection's tolerance."""
     L = w_kv.shape[0]
     if fused:
         h, r = workspace if workspace is not None else (None, None)
@@ -514,6 +533,6 @@ def context_kv_chain(x, hidden_w, pre_w, w_kv, positions, slots, cos_sin, caches
         kv = context_kv_project_fused(h, r, pre_w, w_kv, out=kv, stream=stream)
     else:
         normed = context_norms(x, hidden_w, pre_w, L, hidden_eps, pre_eps, out=workspace, stream=stream)
-        kv = context_kv_project(normed, w_kv, out=kv, stream=stream)
+        kv = context_kv_project(normed, w_kv, out=kv, stream=stream, split=split)
     context_kv_store(kv, positions, slots, cos_sin, caches, H, k_eps, stream=stream)
     return kv

@@ -181,10 +181,12 @@ int32_t nrc_context_kv_project_fused(const uint16_t* h, const float* r, const ui
                          "context_kv_project_fused");
 }
 
-int32_t nrc_context_kv_project_ex(const uint16_t* normed, const uint16_t* w, int32_t w_layout, uint16_t* kv,
-                                  int32_t L, int64_t T, int64_t D, int64_t N, void* stream) {
-    if (w_layout != NRC_KV_WEIGHT_DN && w_layout != NRC_KV_WEIGHT_ND)
-        return fail(NRC_EINVAL, "context_kv_project: weight layout %d (0 [L, D, N], 1 [L, N, D])", w_layout);
+}  // extern "C"
+
+namespace {
+
+// Shape checks shared by the projection entry points (no pointers).
+int32_t project_shape_ok(int32_t L, int64_t T, int64_t D, int64_t N) {
     if (L < 1) return fail(NRC_EINVAL, "context_kv_project: L = %d < 1", L);
     if (T < 0) return fail(NRC_EINVAL, "context_kv_project: T = %lld < 0", (long long)T);
     if (D <= 0 || D % 64) return fail(NRC_ENOTSUP, "context_kv_project: D = %lld is not a positive multiple of 64",
@@ -195,13 +197,58 @@ int32_t nrc_context_kv_project_ex(const uint16_t* normed, const uint16_t* w, int
     if (T > ((int64_t)1 << 31) || D > ((int64_t)1 << 20) || N > ((int64_t)1 << 20) ||
         (int64_t)L * ((T + 127) / 128) * (N / 128) > ((int64_t)1 << 30))
         return fail(NRC_EINVAL, "context_kv_project: shape too large");
+    return NRC_OK;
+}
+
+int64_t project_workspace_bytes(int32_t L, int64_t T, int64_t D, int64_t N) {
+    const int32_t s = nrc::kv_project_k_split(L, T, D, N, num_cus());
+    return s > 1 ? (int64_t)s * L * T * N * 4 : 0;
+}
+
+// The projection behind the entry points; workspace NULL: never split.
+int32_t project_impl(const uint16_t* normed, const uint16_t* w, int32_t w_layout, uint16_t* kv, int32_t L,
+                     int64_t T, int64_t D, int64_t N, void* workspace, int64_t workspace_bytes, bool may_split,
+                     void* stream) {
+    if (w_layout != NRC_KV_WEIGHT_DN && w_layout != NRC_KV_WEIGHT_ND)
+        return fail(NRC_EINVAL, "context_kv_project: weight layout %d (0 [L, D, N], 1 [L, N, D])", w_layout);
+    if (int32_t rc = project_shape_ok(L, T, D, N)) return rc;
     if (T == 0) return NRC_OK;
     if (!normed || !w || !kv) return fail(NRC_EINVAL, "context_kv_project: NULL operand");
     if (!aligned(normed, 16) || !aligned(w, 16) || !aligned(kv, 16))
         return fail(NRC_EINVAL, "context_kv_project: operands must be 16-byte aligned");
     nrc::ProjectArgs a{normed, w, kv, L, T, D, N, num_cus()};
     a.b_nd = w_layout == NRC_KV_WEIGHT_ND;
+    if (may_split) {
+        const int64_t need = project_workspace_bytes(L, T, D, N);
+        if (need > 0) {
+            if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
+                return fail(NRC_EINVAL, "context_kv_project_split: needs a 16-byte aligned workspace of %lld bytes",
+                            (long long)need);
+            a.ws = static_cast<float*>(workspace);
+            a.k_split = nrc::kv_project_k_split(L, T, D, N, a.num_cus);
+        }
+    }
     return launch_status(nrc::launch_kv_project(a, (hipStream_t)stream), "context_kv_project");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t nrc_context_kv_project_ex(const uint16_t* normed, const uint16_t* w, int32_t w_layout, uint16_t* kv,
+                                  int32_t L, int64_t T, int64_t D, int64_t N, void* stream) {
+    return project_impl(normed, w, w_layout, kv, L, T, D, N, nullptr, 0, false, stream);
+}
+
+int64_t nrc_context_kv_project_workspace_bytes(int32_t L, int64_t T, int64_t D, int64_t N) {
+    if (int32_t rc = project_shape_ok(L, T, D, N)) return rc;
+    return T == 0 ? 0 : project_workspace_bytes(L, T, D, N);
+}
+
+int32_t nrc_context_kv_project_split(const uint16_t* normed, const uint16_t* w, int32_t w_layout, uint16_t* kv,
+                                     int32_t L, int64_t T, int64_t D, int64_t N, void* workspace,
+                                     int64_t workspace_bytes, void* stream) {
+    return project_impl(normed, w, w_layout, kv, L, T, D, N, workspace, workspace_bytes, true, stream);
 }
 
 int32_t nrc_context_kv_project(const uint16_t* normed, const uint16_t* w, uint16_t* kv, int32_t L, int64_t T,

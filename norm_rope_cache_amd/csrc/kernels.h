@@ -113,9 +113,14 @@ struct ProjectArgs {
     int64_t M, K, N;
     int32_t num_cus;
     bool b_nd = false;
+    float* ws = nullptr;  // split K: FP32 partial sums [k_split, L, M, N]
+    int32_t k_split = 1;
 };
 
 int launch_kv_project(const ProjectArgs& a, hipStream_t stream);
+// Number of K slices the projection of this shape is split into (1: none):
+// only shapes with too few output tiles to fill the CUs are split.
+int32_t kv_project_k_split(int32_t L, int64_t M, int64_t K, int64_t N, int num_cus);
 // A = bf16((h * |r[m]|) * (gamma_l + center)) built in the kernel; a.A is h [M, K].
 int launch_kv_project_fused(const ProjectArgs& a, const float* r, const uint16_t* gamma, float center,
                             hipStream_t stream);

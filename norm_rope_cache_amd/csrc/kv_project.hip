@@ -105,12 +105,16 @@ struct FusedA {
 // B_ND: the weight is stored [L, N, K] (K contiguous, the pages' storage)
 // instead of [L, K, N]; its tile then takes A's path (64-byte rows per
 // stage, A's swizzle, ds_read_b128 fragments).
-template <int BM, int BN, int WM, int WN, bool FUSED, bool PW, int CMODE, bool B_ND>
+// SPLIT (unfused only): K is cut into k_split slices of K / k_split; tile ids
+// run over (slice, layer, M tile, N tile), and each tile writes its FP32
+// sums to W [k_split, L, M, N] instead of rounding into C.
+template <int BM, int BN, int WM, int WN, bool FUSED, bool PW, int CMODE, bool B_ND, bool SPLIT>
 __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t* __restrict__ A,
                                                               const uint16_t* __restrict__ B,
                                                               uint16_t* __restrict__ C, int64_t M, int64_t K,
                                                               int64_t N, int32_t L, int32_t tiles_m, int32_t tiles_n,
-                                                              int32_t total_tiles, FusedA fa) {
+                                                              int32_t total_tiles, FusedA fa, float* __restrict__ W,
+                                                              int32_t k_split) {
     using CF = Cfg<BM, BN, WM, WN>;
     extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
     lds_char* lds = (lds_char*)lds_raw;
@@ -130,8 +134,9 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
         const int t = (int)blockIdx.x + it * G;
         return t < total_tiles ? t : total_tiles;
     };
-    int layer = 0;
+    int layer = 0, ks = 0;
     int64_t m0 = 0, n0 = 0;
+    const int64_t k_len = SPLIT ? K / k_split : K;  // K walked per tile
     auto decode = [&](int tile) {
         const int tn = tile % tiles_n;
         int tm;
@@ -140,7 +145,9 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
             tm = tile / (tiles_n * L);
         } else {
             tm = (tile / tiles_n) % tiles_m;
-            layer = tile / (tiles_n * tiles_m);
+            const int lt = tile / (tiles_n * tiles_m);
+            layer = SPLIT ? lt % L : lt;
+            ks = SPLIT ? lt / L : 0;
         }
         m0 = (int64_t)tm * BM;
         n0 = (int64_t)tn * BN;
@@ -161,8 +168,9 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     const uint16_t* a_src[CF::A_LOADS];
     const uint16_t* b_src[CF::B_LOADS];
     auto set_sources = [&]() {
-        const uint16_t* Al = FUSED ? A : A + (int64_t)layer * M * K;
-        const uint16_t* Bl = B + (int64_t)layer * K * N;
+        const int64_t k0 = (int64_t)ks * k_len;  // first k of this tile's slice
+        const uint16_t* Al = (FUSED ? A : A + (int64_t)layer * M * K) + k0;
+        const uint16_t* Bl = B + (int64_t)layer * K * N + (B_ND ? k0 : k0 * N);
 #pragma unroll
         for (int t = 0; t < CF::A_LOADS; ++t) {
             const int off = (wave * CF::A_LOADS + t) * 1024 + lane * 16;
@@ -339,7 +347,7 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
         const int i = idx / CF::NI, j = idx % CF::NI;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f][i], bfr[f][j], acc[i][j], 0, 0, 0);
     };
-    const int nk = (int)(K / kBK);
+    const int nk = (int)(k_len / kBK);
     // DMA d (0 .. LOADS-1: A blocks, then B blocks) of stage st into buffer
     // st mod 4. Past the last stage the source is clamped to stage nk - 1 and
     // lands in a buffer nobody reads again, so every iteration issues the
@@ -395,8 +403,9 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     issue_prologue();
     // Epilogue: lane holds column (lane & 31) of each 32 x 32 block, rows
     // 8 (v / 4) + 4 (lane / 32) + (v % 4).
-    auto epilogue = [&](int e_layer, int64_t e_m0, int64_t e_n0) {
+    auto epilogue = [&](int e_layer, int64_t e_m0, int64_t e_n0, int e_ks) {
     uint16_t* Cl = C + (int64_t)e_layer * M * N;
+    float* Wl = W + ((int64_t)e_ks * L + e_layer) * M * N;
     auto store_tile = [&](auto checked) {
 #pragma unroll
         for (int i = 0; i < CF::MI; ++i)
@@ -406,7 +415,11 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int64_t row = e_m0 + wm * CF::WTM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    if (!decltype(checked)::value || row < M) Cl[row * N + col] = (uint16_t)to_bf16(acc[i][j][v]);
+                    if (decltype(checked)::value && row >= M) continue;
+                    if constexpr (SPLIT)
+                        Wl[row * N + col] = acc[i][j][v];
+                    else
+                        Cl[row * N + col] = (uint16_t)to_bf16(acc[i][j][v]);
                 }
             }
     };
@@ -485,7 +498,7 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
         }
         wait_vmcnt<0>();  // the clamped loads past the last stage have landed
         barrier();         // every wave is done with the ring and the weights
-        const int e_layer = layer;
+        const int e_layer = layer, e_ks = ks;
         const int64_t e_m0 = m0, e_n0 = n0;
         const int next = tile_of(++it);
         if (next < total_tiles) {
@@ -494,20 +507,20 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
             set_fused();
             issue_prologue();
         }
-        epilogue(e_layer, e_m0, e_n0);
+        epilogue(e_layer, e_m0, e_n0, e_ks);
         if (next >= total_tiles) break;
     }
     wait_vmcnt<0>();  // no DMA may still target this workgroup's LDS at exit
 }
 
-template <int BM, int BN, int WM, int WN, bool FUSED, bool PW, int CMODE, bool B_ND>
+template <int BM, int BN, int WM, int WN, bool FUSED, bool PW, int CMODE, bool B_ND, bool SPLIT>
 int launch_tiles(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
     using CF = Cfg<BM, BN, WM, WN>;
     const int tiles_m = (int)((a.M + BM - 1) / BM);
     const int tiles_n = (int)(a.N / BN);
-    const int total = a.L * tiles_m * tiles_n;
+    const int total = a.L * tiles_m * tiles_n * (SPLIT ? a.k_split : 1);
     const size_t lds_bytes = CF::LDS_BYTES + ((FUSED && PW) ? (size_t)a.K * 2 : 0);
-    auto kernel = kv_project_kernel<BM, BN, WM, WN, FUSED, PW, CMODE, B_ND>;
+    auto kernel = kv_project_kernel<BM, BN, WM, WN, FUSED, PW, CMODE, B_ND, SPLIT>;
     if (lds_bytes > 65536) {
         static std::atomic<int> done[64] = {};
         if (raise_lds_limit((const void*)kernel, (int)lds_bytes, done)) return -1;
@@ -518,20 +531,78 @@ int launch_tiles(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
     const int cus = a.num_cus > 0 ? a.num_cus : 256;
     const int grid = total < per_cu * cus ? total : per_cu * cus;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(CF::THREADS), lds_bytes, stream, a.A, a.B, a.C, a.M, a.K, a.N, a.L,
-                       tiles_m, tiles_n, total, fa);
+                       tiles_m, tiles_n, total, fa, a.ws, SPLIT ? a.k_split : 1);
     return 0;
+}
+
+// C = bf16(W[0] + W[1] + ... + W[S - 1]) element by element, the slices added
+// in order (deterministic); eight elements per thread, grid stride.
+__global__ __launch_bounds__(256) void kv_project_reduce_kernel(const float* __restrict__ W, uint16_t* __restrict__ C,
+                                                                int64_t count, int32_t S) {
+    for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < count; i += (int64_t)gridDim.x * 256 * 8) {
+        float acc[8];
+        {
+            const U32x4 a = load16(W + i), b = load16(W + i + 4);
+            const uint32_t p[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = __uint_as_float(p[e]);
+        }
+        for (int k = 1; k < S; ++k) {
+            const float* w = W + (int64_t)k * count + i;
+            const U32x4 a = load16(w), b = load16(w + 4);
+            const uint32_t p[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = acc[e] + __uint_as_float(p[e]);
+        }
+        store16(C + i, U32x4{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]), pack_bf16(acc[4], acc[5]),
+                             pack_bf16(acc[6], acc[7])});
+    }
 }
 
 template <bool FUSED, bool PW, int CMODE, bool B_ND>
 int launch_shape(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
-    // 256 x 256 tiles when they fill the chip, else 128 x 128.
+    // 256 x 256 tiles when they fill the chip, else 128 x 128, with K split
+    // when even those are too few (k_split > 1, unfused form only).
     const int64_t big_tiles = (int64_t)a.L * ((a.M + 255) / 256) * (a.N / 256);
     const int cus = a.num_cus > 0 ? a.num_cus : 256;
-    if (a.N % 256 == 0 && big_tiles >= cus) return launch_tiles<256, 256, 2, 4, FUSED, PW, CMODE, B_ND>(a, fa, stream);
-    return launch_tiles<128, 128, 2, 2, FUSED, PW, CMODE, B_ND>(a, fa, stream);
+    if (a.N % 256 == 0 && big_tiles >= cus)
+        return launch_tiles<256, 256, 2, 4, FUSED, PW, CMODE, B_ND, false>(a, fa, stream);
+    if constexpr (!FUSED) {
+        if (a.k_split > 1) {
+            // 256 x 256 slices when the tile is not mostly empty rows (half
+            // the operand traffic per flop of 128 x 128), else 128 x 128
+            const int rc = a.N % 256 == 0 && a.M >= 256
+                               ? launch_tiles<256, 256, 2, 4, false, false, 0, B_ND, true>(a, fa, stream)
+                               : launch_tiles<128, 128, 2, 2, false, false, 0, B_ND, true>(a, fa, stream);
+            if (rc) return rc;
+            const int64_t count = (int64_t)a.L * a.M * a.N;
+            const int64_t blocks = (count / 8 + 255) / 256, cap = (int64_t)cus * 8;
+            hipLaunchKernelGGL(kv_project_reduce_kernel, dim3((unsigned)(blocks < cap ? blocks : cap)), dim3(256), 0,
+                               stream, a.ws, a.C, count, a.k_split);
+            return 0;
+        }
+    }
+    return launch_tiles<128, 128, 2, 2, FUSED, PW, CMODE, B_ND, false>(a, fa, stream);
 }
 
 }  // namespace
+
+int32_t kv_project_k_split(int32_t L, int64_t M, int64_t K, int64_t N, int num_cus) {
+    const int cus = num_cus > 0 ? num_cus : 256;
+    const int64_t big_tiles = (int64_t)L * ((M + 255) / 256) * (N / 256);
+    if (N % 256 == 0 && big_tiles >= cus) return 1;
+    // Slices of 256 x 256 tiles (N a multiple of 256, at least 256 rows) up
+    // to one per CU, else of 128 x 128 tiles up to two per CU (their LDS ring
+    // lets two share a CU); at most 8 slices, each a whole number of at least
+    // 4 stages.
+    const bool big = N % 256 == 0 && M >= 256;
+    const int64_t tiles = big ? big_tiles : (int64_t)L * ((M + 127) / 128) * (N / 128);
+    const int64_t target = big ? (int64_t)cus : 2 * (int64_t)cus;
+    const int64_t nk = K / kBK;
+    int32_t s = 1;
+    while (tiles * s < target && s < 8 && nk % (2 * s) == 0 && nk / (2 * s) >= 4) s *= 2;
+    return s;
+}
 
 int launch_kv_project(const ProjectArgs& a, hipStream_t stream) {
     const int rc = a.b_nd ? launch_shape<false, false, 0, true>(a, FusedA{nullptr, nullptr, 0.0f}, stream)

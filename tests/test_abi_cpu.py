@@ -16,7 +16,7 @@ EINVAL, ENOTSUP = -22, -95
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int32_t|const char\*|void)\s+(nrc_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int32_t|int64_t|const char\*|void)\s+(nrc_\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -152,6 +152,36 @@ def test_project_argument_checks(lib):
     assert f(FAKE, None, FAKE, 1, 8, 8192, 1024, None) == EINVAL
     assert f(FAKE, FAKE, MISALIGNED, 1, 8, 8192, 1024, None) == EINVAL
     assert f(None, None, None, 2, 0, 8192, 1024, None) == 0
+
+
+def test_project_split_workspace_and_argument_checks(lib):
+    """The split form's workspace query (no GPU here: the library assumes 256
+    CUs, as on MI355X) and its argument checks, all before any launch."""
+    q = lib.nrc_context_kv_project_workspace_bytes
+    q.restype = ctypes.c_int64
+    # long workload: 256 x 256 tiles fill the CUs, no split
+    assert q(4, 16384, 8192, 1024) == 0
+    # a 512-row prefill: 32 tiles of 256 x 256, eight slices
+    assert q(4, 512, 8192, 1024) == 8 * 4 * 512 * 1024 * 4
+    # 2000 rows: 128 tiles of 256 x 256, two slices
+    assert q(4, 2000, 8192, 1024) == 2 * 4 * 2000 * 1024 * 4
+    # N = 384: 128 x 128 tiles (18 of them), eight slices
+    assert q(2, 300, 8192, 384) == 8 * 2 * 300 * 384 * 4
+    # 16 rows: eight slices at most
+    assert q(2, 16, 8192, 256) == 8 * 2 * 16 * 256 * 4
+    assert q(4, 0, 8192, 1024) == 0
+    assert q(0, 512, 8192, 1024) == EINVAL
+    assert q(4, 512, 8100, 1024) == ENOTSUP
+    assert q(4, 512, 8192, 1000) == ENOTSUP
+    f = lib.nrc_context_kv_project_split
+    need = 8 * 4 * 512 * 1024 * 4
+    assert f(FAKE, FAKE, 0, FAKE, 4, 512, 8192, 1024, None, need, None) == EINVAL
+    assert "workspace" in _err(lib)
+    assert f(FAKE, FAKE, 0, FAKE, 4, 512, 8192, 1024, FAKE, need - 1, None) == EINVAL
+    assert f(FAKE, FAKE, 0, FAKE, 4, 512, 8192, 1024, MISALIGNED, need, None) == EINVAL
+    assert f(FAKE, FAKE, 2, FAKE, 4, 512, 8192, 1024, FAKE, need, None) == EINVAL
+    assert f(FAKE, FAKE, 0, FAKE, 4, 512, 8192, 1000, FAKE, need, None) == ENOTSUP
+    assert f(None, None, 0, None, 4, 0, 8192, 1024, None, 0, None) == 0
 
 
 def _store(lib, **kw):

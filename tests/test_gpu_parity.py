@@ -466,9 +466,9 @@ def test_new_entry_points_edge_cases(nrc, oracle):
 
 # ---------------------------------------------------------------- projection
 
-def _project_check(nrc, oracle, A, B, rows=None, what=""):
+def _project_check(nrc, oracle, A, B, rows=None, what="", split=True):
     Ad, Bd = to_dev(A), to_dev(B)
-    C = to_host(nrc.context_kv_project(Ad, Bd))
+    C = to_host(nrc.context_kv_project(Ad, Bd, split=split))
     if rows is not None:
         A_s = np.ascontiguousarray(A[:, rows])
         Cstar = oracle.kv_project(A_s, B)
@@ -498,15 +498,67 @@ def test_project_parity_configs(nrc, oracle, name):
 
 
 @pytest.mark.parametrize("T,N", [(1, 128), (5, 256), (37, 1024), (130, 128), (300, 2048), (513, 384), (1000, 1024)])
-def test_project_shapes(nrc, oracle, T, N):
+@pytest.mark.parametrize("split", [True, False])
+def test_project_shapes(nrc, oracle, T, N, split):
+    """Ragged T and several N, with the summation split where the shape has
+    few tiles (split=True, the default) and in one pass."""
     from norm_rope_cache_amd import synth
 
     L = 2
     A = synth.normal_bf16(2000 + T, (L, T, 8192))
     B = synth.normal_bf16(3000 + N, (L, 8192, N), std=0.02)
     rows = None if T <= 64 else np.unique(np.concatenate([[0, T - 1], np.arange(1, T, max(1, T // 40))]))
-    _say(f"project T={T} N={N}")
-    _project_check(nrc, oracle, A, B, rows, f"project T={T} N={N}")
+    _say(f"project T={T} N={N} split={split}")
+    _project_check(nrc, oracle, A, B, rows, f"project T={T} N={N} split={split}", split=split)
+
+
+def _expected_k_split(L, T, N, cus=256, nk=256):
+    """The split rule written out: none when 256 x 256 tiles fill the CUs;
+    else the smallest power of two (at most 8, each slice at least 4 stages
+    of 32) giving one 256 x 256 tile slice per CU (N a multiple of 256, at
+    least 256 rows) or two 128 x 128 tile slices per CU."""
+    big_tiles = L * -(-T // 256) * (N // 256)
+    if N % 256 == 0 and big_tiles >= cus:
+        return 1
+    big = N % 256 == 0 and T >= 256
+    tiles = big_tiles if big else L * -(-T // 128) * (N // 128)
+    target = cus if big else 2 * cus
+    s = 1
+    while tiles * s < target and s < 8 and nk % (2 * s) == 0 and nk // (2 * s) >= 4:
+        s *= 2
+    return s
+
+
+@pytest.mark.parametrize("L,T,N", [(4, 512, 1024), (1, 130, 128), (2, 300, 384), (2, 16, 256), (4, 2000, 1024),
+                                   (1, 700, 512)])
+def test_project_split_summation(nrc, oracle, L, T, N):
+    """Split summation: the workspace the library asks for follows the split
+    rule; the result is within tolerance of the oracle, deterministic, the
+    same bits for both weight layouts, and within tolerance of the one-pass
+    kernel's."""
+    from norm_rope_cache_amd import synth
+
+    lib = nrc._load()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    s = _expected_k_split(L, T, N, cus)
+    want_bytes = s * L * T * N * 4 if s > 1 else 0
+    assert lib.nrc_context_kv_project_workspace_bytes(L, T, 8192, N) == want_bytes
+    A = synth.normal_bf16(4100 + T, (L, T, 8192))
+    B = synth.normal_bf16(4200 + N, (L, 8192, N), std=0.02)
+    Ad, Bd = to_dev(A), to_dev(B)
+    _say(f"project split L={L} T={T} N={N} slices={s}")
+    c1 = to_host(nrc.context_kv_project(Ad, Bd))
+    c2 = to_host(nrc.context_kv_project(Ad, Bd))
+    assert np.array_equal(c1, c2), "split projection not deterministic"
+    Bnd = np.ascontiguousarray(np.swapaxes(B, 1, 2))
+    c_nd = to_host(nrc.context_kv_project(Ad, to_dev(Bnd), w_layout="nd"))
+    assert_bits_equal(c_nd, c1, f"split [L, N, D] vs [L, D, N] {L},{T},{N}")
+    c_one = to_host(nrc.context_kv_project(Ad, Bd, split=False))
+    rows = np.unique(np.concatenate([[0, T - 1], np.arange(1, T, max(1, T // 40))]))
+    Cstar = oracle.kv_project(np.ascontiguousarray(A[:, rows]), B)
+    for c, what in ((c1, "split"), (c_one, "one pass")):
+        ok, msg = projection_tolerance_ok(c[:, rows], Cstar)
+        assert ok, f"{what} L={L} T={T} N={N}: {msg}"
 
 
 @pytest.mark.parametrize("L,T,N", [(4, 3000, 1024), (2, 4196, 2048), (1, 8292, 2560)])
@@ -830,7 +882,7 @@ def test_deterministic(nrc, fused):
         cd = to_dev(d["caches"])
         kv = nrc.context_kv_chain(to_dev(d["x"]), to_dev(d["hidden_w"]), to_dev(d["pre_w"]), to_dev(d["w_kv"]),
                                   to_dev(d["positions"]), to_dev(d["slots"]), to_dev(d["cos_sin"]), cd, cfg.H,
-                                  fused=fused)
+                                  fused=fused, split=False)
         outs.append((to_host(kv), to_host(cd)))
     for a, b in zip(outs[0], outs[1]):
         assert np.array_equal(a, b)
@@ -870,7 +922,7 @@ def _fused_vs_unfused(nrc, x, hw, pw, w_kv, L, he=1e-6, pe=1e-6, hc=0.0, pc=0.0)
     hwd = None if hw is None else to_dev(hw)
     pwd = None if pw is None else to_dev(pw)
     normed = nrc.context_norms(xd, hwd, pwd, L, he, pe, hc, pc)
-    kv_u = nrc.context_kv_project(normed, wd)
+    kv_u = nrc.context_kv_project(normed, wd, split=False)  # one pass, like the fused kernel
     h, r = nrc.context_hidden_norm(xd, hwd, pwd, L, he, pe, hc, pc)
     kv_f = nrc.context_kv_project_fused(h, r, pwd, wd, pc)
     torch.cuda.synchronize()
@@ -943,7 +995,8 @@ def test_fused_project_special_values(nrc):
 
 
 def test_fused_chain_matches_unfused_chain(nrc):
-    """context_kv_chain fused and unfused write identical caches."""
+    """context_kv_chain fused and unfused (one-pass projection) write
+    identical caches."""
     from norm_rope_cache_amd import synth
 
     cfg = synth.scaled(synth.PREFILL, 200)
@@ -953,7 +1006,7 @@ def test_fused_chain_matches_unfused_chain(nrc):
         cd = to_dev(d["caches"])
         kv = nrc.context_kv_chain(to_dev(d["x"]), to_dev(d["hidden_w"]), to_dev(d["pre_w"]), to_dev(d["w_kv"]),
                                   to_dev(d["positions"]), to_dev(d["slots"]), to_dev(d["cos_sin"]), cd, cfg.H,
-                                  fused=fused)
+                                  fused=fused, split=False)
         outs.append((to_host(kv), to_host(cd)))
     assert np.array_equal(outs[0][0], outs[1][0])
     assert np.array_equal(outs[0][1], outs[1][1])
