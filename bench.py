@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+PEAK_CLOCK_GHZ = 2.4           # the engine clock the MFMA peak is quoted at
 
 
 def log(*a):
@@ -232,12 +233,38 @@ def main():
             rec["frac"] = rec["achieved_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS
         rec["traffic_bytes"] = traffic_from_profiles(k)
 
+    # Shader clock of the projection (unfused path): ten more chain steps
+    # whose projection also stamps each workgroup's shader clock and constant
+    # clock counters (the same kernel and bits; the call synchronizes to read
+    # them). The MFMA peak is quoted at 2.4 GHz; under this load the chip
+    # runs slower, and frac_at_clock rates the projection against the peak
+    # scaled to the measured clock.
+    if not fused:
+        clocks = []
+        for _ in range(10):
+            b = sets[step_no[0] % n_sets]
+            step_no[0] += 1
+            nrc.context_norms(b["x"], hw, pw, cfg.L, d["hidden_eps"], d["pre_eps"], out=b["normed"])
+            _, clk = nrc.context_kv_project_timed(b["normed"], b["w"], out=b["kv"])
+            nrc.context_kv_store(b["kv"], positions, slots, cos_sin, b["caches"], cfg.H, d["k_eps"])
+            clocks.append(float(clk["shader_ghz"].median()))
+        torch.cuda.synchronize()
+        ghz = sorted(clocks)[len(clocks) // 2]
+        rec = kernels[n1]
+        rec["clock_ghz"] = ghz
+        rec["frac_at_clock"] = rec["achieved_TFLOPs"] / (BF16_MFMA_PEAK_TFLOPS * ghz / PEAK_CLOCK_GHZ)
+        log(f"projection shader clock {ghz:.3f} GHz (median of {len(clocks)} launches' workgroup medians); "
+            f"{rec['frac_at_clock']:.3f} of the MFMA peak at that clock")
+
     # the dominant kernel (longest launch) carries the roofline object
     dom = max(avg, key=avg.get)
     rd = kernels[dom]
     if rd["bound"] == "mfma":
         roofline = {"bound": "mfma", "achieved": rd["achieved_TFLOPs"], "peak": BF16_MFMA_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": rd["frac"], "traffic": rd["traffic_bytes"], "kernel": dom}
+        if "clock_ghz" in rd:
+            roofline["clock_ghz"] = rd["clock_ghz"]
+            roofline["frac_at_clock"] = rd["frac_at_clock"]
     else:
         roofline = {"bound": "hbm", "achieved": rd["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": rd["frac"], "traffic": rd["traffic_bytes"], "kernel": dom}
@@ -252,7 +279,7 @@ def main():
     # cache would keep most of the 268 MB input between launches (nontemporal
     # outputs do not evict it), which the chain never sees.
     def time_launches(run, flush_src, warmup=20, timed=20):
-        flush_dst = torch.empty(1, dtype=torch.float32, device=dev)
+        flush_dst = torch.empty((), dtype=torch.float32, device=dev)
         for _ in range(warmup):
             run()
         total = 0.0

@@ -205,6 +205,32 @@ int32_t nrc_context_kv_project_split(const uint16_t* normed, const uint16_t* w, 
                                      int64_t workspace_bytes, void* stream);
 
 /*
+ * nrc_context_kv_project_timed - nrc_context_kv_project_ex (one pass, never
+ * split) that also records, per workgroup, the shader clock counter
+ * (s_memtime) and the constant-rate counter (s_memrealtime) when the
+ * workgroup starts and when it ends. A diagnostic for callers that want the
+ * clock the matrix cores ran at: (end - start) of the first counter over
+ * that of the second, times the constant rate. Same operation and bits as
+ * nrc_context_kv_project_ex (page "...runtime.draft", ContextKV._project).
+ *
+ *   stamps      caller-owned device memory, 8-byte aligned, uint64
+ *               [stamps_len]; workgroup g writes stamps[4 g .. 4 g + 3] =
+ *               shader clock at start, constant clock at start, shader
+ *               clock at end, constant clock at end. Other entries untouched.
+ *   stamps_len  its length in elements, at least nrc_context_kv_project_timed
+ *               needs: 8 times the device's compute unit count.
+ *   workgroups  host int32: receives the number of workgroups launched
+ *               (each writes its 4 stamps).
+ *   wall_khz    host int32: receives the constant counter's rate in kHz.
+ *   Other arguments and errors as nrc_context_kv_project_ex, plus NRC_EINVAL
+ *   for NULL or misaligned stamps, a short stamps_len, or NULL host outputs.
+ *   T == 0: returns 0 with *workgroups = 0 and launches nothing.
+ */
+int32_t nrc_context_kv_project_timed(const uint16_t* normed, const uint16_t* w, int32_t w_layout, uint16_t* kv,
+                                     int32_t L, int64_t T, int64_t D, int64_t N, uint64_t* stamps,
+                                     int64_t stamps_len, int32_t* workgroups, int32_t* wall_khz, void* stream);
+
+/*
  * nrc_context_hidden_norm - the pre-pass of the fused norms + projection: the
  * hidden norm and each row's layer-norm scale, the two quantities every
  * layer norm of a row shares. Page "...cutedsl.draft.context", ContextNorms

@@ -93,6 +93,9 @@ def _load():
     L.nrc_context_kv_project_workspace_bytes.argtypes = [_i32, _i64, _i64, _i64]
     L.nrc_context_kv_project_split.restype = _i32
     L.nrc_context_kv_project_split.argtypes = [_vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp]
+    L.nrc_context_kv_project_timed.restype = _i32
+    L.nrc_context_kv_project_timed.argtypes = [_vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _vp,
+                                               _vp]
     L.nrc_context_kv_store.restype = _i32
     L.nrc_context_kv_store.argtypes = [
         _vp, _vp, _i64, _i64, _i64, _i64, _vp, ctypes.POINTER(_vp), _i64, _i64, _vp, _i64,
@@ -322,12 +325,8 @@ def context_kv_project_fused(h, r, pre_w, w_kv, pre_center=0.0, out=None, stream
     return out
 
 
-def context_kv_project(normed, w_kv, out=None, stream=None, w_layout="dn", split=True):
-    """[L, T, D] x [L, D, N] -> [L, T, N] bf16 (FP32 accumulation).
-    w_layout "nd": w_kv is stored [L, N, D] (the pages' storage). split: for
-    shapes with too few output tiles to fill the GPU (small T) the summation
-    axis is split over several workgroups, with a workspace from torch's
-    allocator (split=False keeps the one-pass kernel)."""
+def _project_operands(normed, w_kv, out, w_layout):
+    """Shape checks of the projection; returns L, T, D, N, the layout code and out."""
     import torch
 
     _bf16(normed, "normed")
@@ -349,8 +348,19 @@ def context_kv_project(normed, w_kv, out=None, stream=None, w_layout="dn", split
         _bf16(out, "out")
         if tuple(out.shape) != (L, T, N):
             raise ValueError("out must be [L, T, N]")
+    return L, T, D, N, (0 if w_layout == "dn" else 1), out
+
+
+def context_kv_project(normed, w_kv, out=None, stream=None, w_layout="dn", split=True):
+    """[L, T, D] x [L, D, N] -> [L, T, N] bf16 (FP32 accumulation).
+    w_layout "nd": w_kv is stored [L, N, D] (the pages' storage). split: for
+    shapes with too few output tiles to fill the GPU (small T) the summation
+    axis is split over several workgroups, with a workspace from torch's
+    allocator (split=False keeps the one-pass kernel)."""
+    import torch
+
+    L, T, D, N, layout, out = _project_operands(normed, w_kv, out, w_layout)
     lib = _load()
-    layout = 0 if w_layout == "dn" else 1
     need = lib.nrc_context_kv_project_workspace_bytes(L, T, D, N) if split else 0
     if need < 0:
         _check(need)
@@ -365,6 +375,31 @@ def context_kv_project(normed, w_kv, out=None, stream=None, w_layout="dn", split
     else:
         _check(lib.nrc_context_kv_project_ex(_ptr(normed), _ptr(w_kv), 1, _ptr(out), L, T, D, N, _stream(stream)))
     return out
+
+
+def context_kv_project_timed(normed, w_kv, out=None, stream=None, w_layout="dn"):
+    """The one-pass projection with per-workgroup clock stamps (a diagnostic;
+    the call synchronizes the device to read them). Returns (out, clocks):
+    clocks holds 'workgroups', 'stamps' (CPU int64 [workgroups, 4]: shader
+    clock at start, constant clock at start, shader clock at end, constant
+    clock at end), 'wall_khz' (the constant clock's rate) and 'shader_ghz'
+    (each workgroup's mean shader clock over its lifetime, GHz)."""
+    import ctypes
+    import torch
+
+    L, T, D, N, layout, out = _project_operands(normed, w_kv, out, w_layout)
+    lib = _load()
+    n = 8 * torch.cuda.get_device_properties(normed.device).multi_processor_count
+    stamps = torch.zeros(n, dtype=torch.int64, device=normed.device)
+    wg, khz = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib.nrc_context_kv_project_timed(_ptr(normed), _ptr(w_kv), layout, _ptr(out), L, T, D, N, _ptr(stamps),
+                                            n, ctypes.byref(wg), ctypes.byref(khz), _stream(stream)))
+    torch.cuda.synchronize(normed.device)
+    st = stamps[: 4 * wg.value].view(-1, 4).cpu()
+    ds = (st[:, 2] - st[:, 0]).double()
+    dr = (st[:, 3] - st[:, 1]).double()
+    ghz = (ds / dr * khz.value / 1e6) if wg.value else torch.empty(0, dtype=torch.float64)
+    return out, {"workgroups": wg.value, "stamps": st, "wall_khz": khz.value, "shader_ghz": ghz}
 
 
 def kv_views(kv, H):

@@ -251,6 +251,36 @@ int32_t nrc_context_kv_project_split(const uint16_t* normed, const uint16_t* w, 
     return project_impl(normed, w, w_layout, kv, L, T, D, N, workspace, workspace_bytes, true, stream);
 }
 
+int32_t nrc_context_kv_project_timed(const uint16_t* normed, const uint16_t* w, int32_t w_layout, uint16_t* kv,
+                                     int32_t L, int64_t T, int64_t D, int64_t N, uint64_t* stamps,
+                                     int64_t stamps_len, int32_t* workgroups, int32_t* wall_khz, void* stream) {
+    if (!workgroups || !wall_khz) return fail(NRC_EINVAL, "context_kv_project_timed: NULL host output");
+    *workgroups = 0;
+    if (w_layout != NRC_KV_WEIGHT_DN && w_layout != NRC_KV_WEIGHT_ND)
+        return fail(NRC_EINVAL, "context_kv_project: weight layout %d (0 [L, D, N], 1 [L, N, D])", w_layout);
+    if (int32_t rc = project_shape_ok(L, T, D, N)) return rc;
+    const int cus = num_cus();
+    // At most two workgroups per CU (the 128 x 128 tiles' LDS ring), 4 stamps each.
+    if (!stamps || !aligned(stamps, 8) || stamps_len < 8 * (int64_t)cus)
+        return fail(NRC_EINVAL, "context_kv_project_timed: stamps must be 8-byte aligned with at least %lld entries",
+                    (long long)(8 * (int64_t)cus));
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+        return fail(NRC_EIO, "context_kv_project_timed: no constant clock rate for the current device");
+    *wall_khz = khz;
+    if (T == 0) return NRC_OK;
+    if (!normed || !w || !kv) return fail(NRC_EINVAL, "context_kv_project: NULL operand");
+    if (!aligned(normed, 16) || !aligned(w, 16) || !aligned(kv, 16))
+        return fail(NRC_EINVAL, "context_kv_project: operands must be 16-byte aligned");
+    nrc::ProjectArgs a{normed, w, kv, L, T, D, N, cus};
+    a.b_nd = w_layout == NRC_KV_WEIGHT_ND;
+    a.stamps = stamps;
+    a.stamps_len = stamps_len;
+    a.workgroups = workgroups;
+    return launch_status(nrc::launch_kv_project(a, (hipStream_t)stream), "context_kv_project_timed");
+}
+
 int32_t nrc_context_kv_project(const uint16_t* normed, const uint16_t* w, uint16_t* kv, int32_t L, int64_t T,
                                int64_t D, int64_t N, void* stream) {
     return nrc_context_kv_project_ex(normed, w, NRC_KV_WEIGHT_DN, kv, L, T, D, N, stream);

@@ -115,6 +115,12 @@ struct ProjectArgs {
     bool b_nd = false;
     float* ws = nullptr;  // split K: FP32 partial sums [k_split, L, M, N]
     int32_t k_split = 1;
+    // Diagnostic clock stamps, 4 per workgroup (shader clock and constant-rate
+    // clock at the start, then at the end), written when non-null; unfused,
+    // unsplit form only. *workgroups receives the grid size when non-null.
+    uint64_t* stamps = nullptr;
+    int64_t stamps_len = 0;
+    int32_t* workgroups = nullptr;
 };
 
 int launch_kv_project(const ProjectArgs& a, hipStream_t stream);

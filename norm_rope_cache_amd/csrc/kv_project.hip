@@ -114,8 +114,18 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
                                                               uint16_t* __restrict__ C, int64_t M, int64_t K,
                                                               int64_t N, int32_t L, int32_t tiles_m, int32_t tiles_n,
                                                               int32_t total_tiles, FusedA fa, float* __restrict__ W,
-                                                              int32_t k_split) {
+                                                              int32_t k_split, uint64_t* __restrict__ stamps,
+                                                              int64_t stamps_len) {
     using CF = Cfg<BM, BN, WM, WN>;
+    // Clock stamps (diagnostic, stamps non-null): the shader clock counter
+    // and the constant-rate counter when the workgroup starts; the wait keeps
+    // the scalar reads from staying outstanding into the loop.
+    uint64_t clk_s0 = 0, clk_r0 = 0;
+    if (stamps != nullptr) {
+        clk_s0 = __builtin_amdgcn_s_memtime();
+        clk_r0 = __builtin_amdgcn_s_memrealtime();
+        wait_lgkmcnt0();
+    }
     extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
     lds_char* lds = (lds_char*)lds_raw;
 
@@ -511,6 +521,14 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
         if (next >= total_tiles) break;
     }
     wait_vmcnt<0>();  // no DMA may still target this workgroup's LDS at exit
+    if (stamps != nullptr && threadIdx.x == 0 && 4 * (int64_t)blockIdx.x + 3 < stamps_len) {
+        const uint64_t clk_s1 = __builtin_amdgcn_s_memtime(), clk_r1 = __builtin_amdgcn_s_memrealtime();
+        uint64_t* p = stamps + 4 * (int64_t)blockIdx.x;
+        p[0] = clk_s0;
+        p[1] = clk_r0;
+        p[2] = clk_s1;
+        p[3] = clk_r1;
+    }
 }
 
 template <int BM, int BN, int WM, int WN, bool FUSED, bool PW, int CMODE, bool B_ND, bool SPLIT>
@@ -531,7 +549,8 @@ int launch_tiles(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
     const int cus = a.num_cus > 0 ? a.num_cus : 256;
     const int grid = total < per_cu * cus ? total : per_cu * cus;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(CF::THREADS), lds_bytes, stream, a.A, a.B, a.C, a.M, a.K, a.N, a.L,
-                       tiles_m, tiles_n, total, fa, a.ws, SPLIT ? a.k_split : 1);
+                       tiles_m, tiles_n, total, fa, a.ws, SPLIT ? a.k_split : 1, a.stamps, a.stamps_len);
+    if (a.workgroups) *a.workgroups = grid;
     return 0;
 }
 

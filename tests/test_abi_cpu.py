@@ -184,6 +184,26 @@ def test_project_split_workspace_and_argument_checks(lib):
     assert f(None, None, 0, None, 4, 0, 8192, 1024, None, 0, None) == 0
 
 
+def test_project_timed_argument_checks(lib):
+    """The clock-stamped projection rejects bad host outputs, stamps and shapes
+    before touching a device (no GPU here: the library assumes 256 CUs, so
+    8 * 256 stamps are required)."""
+    f = lib.nrc_context_kv_project_timed
+    wg, khz = ctypes.c_int32(7), ctypes.c_int32(0)
+    n = 8 * 256
+    assert f(FAKE, FAKE, 0, FAKE, 4, 512, 8192, 1024, FAKE, n, None, ctypes.byref(khz), None) == EINVAL
+    assert f(FAKE, FAKE, 0, FAKE, 4, 512, 8192, 1024, FAKE, n, ctypes.byref(wg), None, None) == EINVAL
+    assert f(FAKE, FAKE, 2, FAKE, 4, 512, 8192, 1024, FAKE, n, ctypes.byref(wg), ctypes.byref(khz), None) == EINVAL
+    assert wg.value == 0, "workgroups is cleared on every call"
+    assert f(FAKE, FAKE, 0, FAKE, 4, 512, 8192, 1000, FAKE, n, ctypes.byref(wg), ctypes.byref(khz), None) == ENOTSUP
+    assert f(FAKE, FAKE, 0, FAKE, 0, 512, 8192, 1024, FAKE, n, ctypes.byref(wg), ctypes.byref(khz), None) == EINVAL
+    assert f(FAKE, FAKE, 0, FAKE, 4, 512, 8192, 1024, None, n, ctypes.byref(wg), ctypes.byref(khz), None) == EINVAL
+    assert "stamps" in _err(lib)
+    odd = ctypes.c_void_p(0x10004)  # 4- but not 8-byte aligned
+    assert f(FAKE, FAKE, 0, FAKE, 4, 512, 8192, 1024, odd, n, ctypes.byref(wg), ctypes.byref(khz), None) == EINVAL
+    assert f(FAKE, FAKE, 0, FAKE, 4, 512, 8192, 1024, FAKE, n - 1, ctypes.byref(wg), ctypes.byref(khz), None) == EINVAL
+    assert str(n) in _err(lib)
+
 def _store(lib, **kw):
     a = dict(k=FAKE, v=FAKE, kls=1024 * 16, krs=1024, vls=1024 * 16, vrs=1024, pos=FAKE, slots=None, rows=16,
              T=16, cs=FAKE, maxp=4096, caches=None, nb=64, bs=16, H=8, L=2, eps=1e-6)

@@ -561,6 +561,34 @@ def test_project_split_summation(nrc, oracle, L, T, N):
         assert ok, f"{what} L={L} T={T} N={N}: {msg}"
 
 
+
+@pytest.mark.parametrize("L,T,N", [(4, 512, 1024), (2, 300, 384), (4, 16384, 1024)])
+def test_project_timed_matches_and_stamps(nrc, L, T, N):
+    """The clock-stamped projection gives the one-pass kernel's bits, launches
+    one workgroup per CU (256 x 256 tiles) or up to two (128 x 128), and every
+    workgroup's stamps run forward at a plausible shader clock."""
+    from norm_rope_cache_amd import synth
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    A = to_dev(synth.normal_bf16(4300 + T, (L, T, 8192)))
+    B = to_dev(synth.normal_bf16(4400 + N, (L, 8192, N), std=0.02))
+    _say(f"project timed L={L} T={T} N={N}")
+    ref = to_host(nrc.context_kv_project(A, B, split=False))
+    out, clk = nrc.context_kv_project_timed(A, B)
+    assert_bits_equal(to_host(out), ref, f"timed projection {L},{T},{N}")
+    big = N % 256 == 0 and L * ((T + 255) // 256) * (N // 256) >= cus
+    tiles = L * ((T + 255) // 256) * (N // 256) if big else L * ((T + 127) // 128) * (N // 128)
+    assert clk["workgroups"] == min(tiles, cus if big else 2 * cus)
+    st = clk["stamps"]
+    assert st.shape == (clk["workgroups"], 4)
+    assert bool((st[:, 2] > st[:, 0]).all()) and bool((st[:, 3] > st[:, 1]).all())
+    assert clk["wall_khz"] > 0
+    ghz = clk["shader_ghz"]
+    assert float(ghz.min()) > 0.05 and float(ghz.max()) < 5.0, (float(ghz.min()), float(ghz.max()))
+    _say(f"  shader clock GHz median {float(ghz.median()):.3f}")
+    z, clk0 = nrc.context_kv_project_timed(A[:, :0], B)
+    assert clk0["workgroups"] == 0 and z.shape == (L, 0, N)
+
 @pytest.mark.parametrize("L,T,N", [(4, 3000, 1024), (2, 4196, 2048), (1, 8292, 2560)])
 def test_project_several_tiles_per_workgroup(nrc, oracle, L, T, N):
     """Shapes with more output tiles than resident workgroups, so each
