@@ -10,52 +10,34 @@
 // with fully coalesced 128-byte runs and the fold's three cross-lane strides
 // are DPP / swizzle exchanges inside each 8-lane group.
 //
-// Work unit u = (layer, row, head) with the head fastest; lanes 8u .. 8u+7.
-// Rows whose slot is negative (or out of range, or whose position is out of
-// range), and rows past their layer's slot list, read nothing and write
-// nothing. The cache is a strided view: (block, page, head) at block *
-// block_stride + page * page_stride + head * head_stride, K in the first 64
-// elements of the 128-element run and V in the next 64.
+// Work unit u = (layer, row, head) with the head fastest, taken by an
+// 8-lane group (lanes 8u .. 8u+7). Rows whose slot is negative (or out of
+// range, or whose position is out of range), and rows past their layer's
+// slot list, read nothing but their slot and position and write nothing.
+// The cache is a strided view: (block, page, head) at block * block_stride +
+// page * page_stride + head * head_stride, K in the first 64 elements of the
+// 128-element run and V in the next 64.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace nrc {
 
+typedef __attribute__((address_space(1))) const int64_t GlobalI64;
+typedef __attribute__((address_space(1))) uint16_t GlobalU16;
+
+// 16-byte non-temporal store through a global-memory pointer.
+__device__ __forceinline__ void store16_nt_global(GlobalU16* p, U32x4 v) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, (__attribute__((address_space(1))) u32x4*)p);
+}
+
+// The K-norm, RoPE and packing of one lane's 8 elements of K (the fold's
+// lane exchanges stay inside the lane's 8-lane group). Each rounding to bf16
+// takes the paired hardware conversion when its inputs cannot be NaN (equal
+// to the exact rounding for every other input), else the exact one.
 template <bool ROPE>
-__global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                                                       int64_t k_ls, int64_t k_rs, int64_t v_ls, int64_t v_rs,
-                                                       const int64_t* __restrict__ positions,
-                                                       const uint16_t* __restrict__ cos_sin, int64_t max_position,
-                                                       StoreLayers layers, uint32_t rows, uint32_t H,
-                                                       uint32_t log2H, uint32_t total_units, uint32_t block_size,
-                                                       int32_t bs_shift, uint32_t n_slots, int64_t block_stride,
-                                                       int64_t page_stride, int64_t head_stride, float eps) {
-    const uint32_t unit = (blockIdx.x * blockDim.x + threadIdx.x) >> 3;
-    const uint32_t g = threadIdx.x & 7u;  // this lane's 8 elements of the head: 8g .. 8g+7
-    if (unit >= total_units) return;  // whole 8-lane groups leave together
-    const uint32_t h = unit & (H - 1u);
-    const uint32_t rt = unit >> log2H;
-    const uint32_t l = rt / rows;
-    const uint32_t t = rt - l * rows;
-
-    if (t >= layers.rows[l]) return;  // past this layer's slot list (or a layer without one)
-    const int64_t slot = layers.slots[l][t];
-    if (slot < 0 || (uint64_t)slot >= (uint64_t)n_slots) return;
-    const uint16_t* cs = nullptr;
-    if constexpr (ROPE) {
-        const int64_t p = positions[t];
-        if (p < 0 || p >= max_position) return;
-        cs = cos_sin + p * kHeadDim;
-    }
-
-    const U32x4 kw = load16(k + (int64_t)l * k_ls + (int64_t)t * k_rs + h * kHeadDim + 8 * g);
-    const U32x4 vw = load16(v + (int64_t)l * v_ls + (int64_t)t * v_rs + h * kHeadDim + 8 * g);
-    uint2 cw, sw;
-    if constexpr (ROPE) {
-        cw = *reinterpret_cast<const uint2*>(cs + 4 * g);                  // cos of pairs 4g .. 4g+3
-        sw = *reinterpret_cast<const uint2*>(cs + kHeadDim / 2 + 4 * g);   // sin of the same pairs
-    }
-
+__device__ __forceinline__ U32x4 k_out(U32x4 kw, uint2 cw, uint2 sw, float eps) {
     float kf[8] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y),
                    bf16_lo(kw.z), bf16_hi(kw.z), bf16_lo(kw.w), bf16_hi(kw.w)};
     float q[8];
@@ -77,27 +59,113 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restric
     const float S = q[0] + q[1];
     const float r = rsqrt_rn(__builtin_fmaf(S, 0.015625f, eps));  // mean: 1/64 exact
 
-    uint32_t nb[8];
+    float y[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) nb[i] = to_bf16(kf[i] * r);
-
-    U32x4 out;
-    if constexpr (ROPE) {
+    for (int i = 0; i < 8; ++i) y[i] = kf[i] * r;
+    // A finite S means every k is finite; with r finite too, no k * r is NaN.
+    uint32_t nb[4];
+    if (__builtin_isfinite(S) && __builtin_isfinite(r)) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) nb[p] = pack_bf16_pair_hw(y[2 * p], y[2 * p + 1]);
+    } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) nb[p] = pack_bf16(y[2 * p], y[2 * p + 1]);
+    }
+    if constexpr (!ROPE) {
+        return U32x4{nb[0], nb[1], nb[2], nb[3]};
+    } else {
         const float c[4] = {bf16_lo(cw.x), bf16_hi(cw.x), bf16_lo(cw.y), bf16_hi(cw.y)};
         const float s[4] = {bf16_lo(sw.x), bf16_hi(sw.x), bf16_lo(sw.y), bf16_hi(sw.y)};
-        uint32_t o[4];
+        float z[8];
+        bool nan = false;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const float a = __uint_as_float(nb[2 * p] << 16);
-            const float b = __uint_as_float(nb[2 * p + 1] << 16);
+            const float a = bf16_lo(nb[p]);
+            const float b = bf16_hi(nb[p]);
             const float bs = b * s[p];
             const float as = a * s[p];
-            o[p] = to_bf16(__builtin_fmaf(a, c[p], -bs)) | (to_bf16(__builtin_fmaf(b, c[p], as)) << 16);
+            z[2 * p] = __builtin_fmaf(a, c[p], -bs);
+            z[2 * p + 1] = __builtin_fmaf(b, c[p], as);
+            nan = nan || __builtin_isnan(z[2 * p]) || __builtin_isnan(z[2 * p + 1]);
         }
-        out = U32x4{o[0], o[1], o[2], o[3]};
-    } else {
-        out = U32x4{nb[0] | (nb[1] << 16), nb[2] | (nb[3] << 16), nb[4] | (nb[5] << 16), nb[6] | (nb[7] << 16)};
+        uint32_t o[4];
+        if (!nan) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) o[p] = pack_bf16_pair_hw(z[2 * p], z[2 * p + 1]);
+        } else {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) o[p] = pack_bf16(z[2 * p], z[2 * p + 1]);
+        }
+        return U32x4{o[0], o[1], o[2], o[3]};
     }
+}
+
+// One 8-lane group per work unit. ROW_WAVE (H >= 8): a wave's 8 groups are 8
+// heads of one (layer, row), so the layer, the row, its slot and position and
+// the K/V row bases are wave-uniform and computed once, in scalar registers;
+// only the head offset is per lane. Otherwise (H < 8) a wave spans 8 / H
+// rows, possibly of two layers, and each lane works them out itself.
+template <bool ROPE, bool ROW_WAVE>
+__global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                       int64_t k_ls, int64_t k_rs, int64_t v_ls, int64_t v_rs,
+                                                       const int64_t* __restrict__ positions,
+                                                       const uint16_t* __restrict__ cos_sin, int64_t max_position,
+                                                       StoreLayers layers, uint32_t rows, uint32_t H,
+                                                       uint32_t log2H, uint32_t total_units, uint32_t block_size,
+                                                       int32_t bs_shift, uint32_t n_slots, int64_t block_stride,
+                                                       int64_t page_stride, int64_t head_stride, float eps) {
+    const uint32_t unit = (blockIdx.x * blockDim.x + threadIdx.x) >> 3;
+    const uint32_t g = threadIdx.x & 7u;  // this lane's 8 elements of the head: 8g .. 8g+7
+    const uint32_t h = unit & (H - 1u);
+    // With ROW_WAVE the unit count is a multiple of 8, so whole waves leave;
+    // otherwise whole 8-lane groups.
+    if (unit >= total_units) return;
+    uint32_t rt;
+    if constexpr (ROW_WAVE)
+        rt = __builtin_amdgcn_readfirstlane(unit) >> log2H;  // the wave's (layer, row)
+    else
+        rt = unit >> log2H;
+    const uint32_t l = rt / rows;
+    const uint32_t t = rt - l * rows;
+
+    // The layers' operands, held in scalar registers and picked by compares
+    // (uniform with ROW_WAVE, per lane otherwise): indexing the argument
+    // arrays by l would be a memory load, one more round trip ahead of the
+    // row's own loads. The empty asm statements keep the compiler from
+    // folding the selection back into such a load.
+    uint32_t l_rows = 0;
+    uint64_t l_slots_a = 0, l_cache_a = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < (uint32_t)kMaxLayersPerLaunch; ++i) {
+        uint32_t ri = layers.rows[i];
+        uint64_t si = (uint64_t)(uintptr_t)layers.slots[i];
+        uint64_t ci = (uint64_t)(uintptr_t)layers.cache[i];
+        asm volatile("" : "+s"(ri), "+s"(si), "+s"(ci));
+        if (l == i) {
+            l_rows = ri;
+            l_slots_a = si;
+            l_cache_a = ci;
+        }
+    }
+    if (t >= l_rows) return;  // past this layer's slot list (or a layer without one)
+    // The slot and the position (every row below rows has one) in one round
+    // trip, tested together; K, V and the cos/sin row in a second.
+    const int64_t slot = ((const GlobalI64*)l_slots_a)[t];  // a device allocation: global memory
+    const int64_t pos = ROPE ? positions[t] : 0;
+    // (bitwise &: both loads are needed before the one test)
+    const bool slot_ok = (slot >= 0) & ((uint64_t)slot < (uint64_t)n_slots);
+    const bool pos_ok = !ROPE || ((pos >= 0) & (pos < max_position));
+    if (!(slot_ok & pos_ok)) return;
+
+    const U32x4 kw = load16(k + (int64_t)l * k_ls + (int64_t)t * k_rs + h * kHeadDim + 8 * g);
+    const U32x4 vw = load16(v + (int64_t)l * v_ls + (int64_t)t * v_rs + h * kHeadDim + 8 * g);
+    uint2 cw = {0u, 0u}, sw = {0u, 0u};
+    if constexpr (ROPE) {
+        const uint16_t* cs = cos_sin + pos * kHeadDim;
+        cw = *reinterpret_cast<const uint2*>(cs + 4 * g);                  // cos of pairs 4g .. 4g+3
+        sw = *reinterpret_cast<const uint2*>(cs + kHeadDim / 2 + 4 * g);   // sin of the same pairs
+    }
+    const U32x4 out = k_out<ROPE>(kw, cw, sw, eps);
 
     // Slots fit 32 bits (checked on the host): block = s / block_size, page = s % block_size.
     const uint32_t s32 = (uint32_t)slot;
@@ -109,29 +177,31 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restric
         block = s32 / block_size;
         page = s32 - block * block_size;
     }
-    uint16_t* dst = layers.cache[l] + (int64_t)block * block_stride + (int64_t)page * page_stride +
-                    (int64_t)h * head_stride + 8 * g;
+    GlobalU16* dst = (GlobalU16*)l_cache_a + (int64_t)block * block_stride + (int64_t)page * page_stride +
+                     (int64_t)h * head_stride + 8 * g;
     // Non-temporal: the cache rows are scattered and not read back by this
     // chain, so they go out to HBM now instead of lingering dirty in the
     // caches until the next kernel's traffic evicts them.
-    store16_nt(dst, out);
-    store16_nt(dst + kHeadDim, vw);
+    store16_nt_global(dst, out);
+    store16_nt_global(dst + kHeadDim, vw);
+}
+
+template <bool ROPE>
+void launch_rope(const KvStoreArgs& a, uint32_t total_units, hipStream_t stream) {
+    const uint32_t threads = 256;
+    const uint32_t blocks = (uint32_t)(((uint64_t)total_units * 8 + threads - 1) / threads);
+    auto kernel = a.H >= 8 ? kv_store_kernel<ROPE, true> : kv_store_kernel<ROPE, false>;
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(threads), 0, stream, a.k, a.v, a.k_ls, a.k_rs, a.v_ls, a.v_rs,
+                       a.positions, a.cos_sin, a.max_position, a.layers, a.rows, a.H, a.log2H, total_units,
+                       a.block_size, a.bs_shift, a.n_slots, a.block_stride, a.page_stride, a.head_stride, a.eps);
 }
 
 int launch_kv_store(const KvStoreArgs& a, hipStream_t stream) {
     const uint32_t total_units = (uint32_t)a.layers_in_launch * a.rows * a.H;
-    const uint32_t threads = 256;
-    const uint32_t blocks = (uint32_t)(((uint64_t)total_units * 8 + threads - 1) / threads);
     if (a.cos_sin)
-        hipLaunchKernelGGL(kv_store_kernel<true>, dim3(blocks), dim3(threads), 0, stream, a.k, a.v, a.k_ls, a.k_rs,
-                           a.v_ls, a.v_rs, a.positions, a.cos_sin, a.max_position, a.layers, a.rows, a.H, a.log2H,
-                           total_units, a.block_size, a.bs_shift, a.n_slots, a.block_stride, a.page_stride,
-                           a.head_stride, a.eps);
+        launch_rope<true>(a, total_units, stream);
     else
-        hipLaunchKernelGGL(kv_store_kernel<false>, dim3(blocks), dim3(threads), 0, stream, a.k, a.v, a.k_ls, a.k_rs,
-                           a.v_ls, a.v_rs, a.positions, a.cos_sin, a.max_position, a.layers, a.rows, a.H, a.log2H,
-                           total_units, a.block_size, a.bs_shift, a.n_slots, a.block_stride, a.page_stride,
-                           a.head_stride, a.eps);
+        launch_rope<false>(a, total_units, stream);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
