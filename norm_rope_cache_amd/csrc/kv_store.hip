@@ -100,11 +100,12 @@ __device__ __forceinline__ U32x4 k_out(U32x4 kw, uint2 cw, uint2 sw, float eps) 
     }
 }
 
-// One 8-lane group per work unit. ROW_WAVE (H >= 8): a wave's 8 groups are 8
-// heads of one (layer, row), so the layer, the row, its slot and position and
-// the K/V row bases are wave-uniform and computed once, in scalar registers;
-// only the head offset is per lane. Otherwise (H < 8) a wave spans 8 / H
-// rows, possibly of two layers, and each lane works them out itself.
+// One 8-lane group per work unit. ROW_WAVE (H >= 8): the grid is (waves of
+// rows, layers) and a wave's 8 groups are 8 heads of one row, so the layer,
+// the row, its slot and position and the K/V row bases are wave-uniform and
+// computed once, in scalar registers; only the head offset is per lane.
+// Otherwise (H < 8) a wave spans 8 / H rows, possibly of two layers, and
+// each lane works them out itself.
 template <bool ROPE, bool ROW_WAVE>
 __global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                        int64_t k_ls, int64_t k_rs, int64_t v_ls, int64_t v_rs,
@@ -114,37 +115,45 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restric
                                                        uint32_t log2H, uint32_t total_units, uint32_t block_size,
                                                        int32_t bs_shift, uint32_t n_slots, int64_t block_stride,
                                                        int64_t page_stride, int64_t head_stride, float eps) {
-    const uint32_t unit = (blockIdx.x * blockDim.x + threadIdx.x) >> 3;
     const uint32_t g = threadIdx.x & 7u;  // this lane's 8 elements of the head: 8g .. 8g+7
-    const uint32_t h = unit & (H - 1u);
-    // With ROW_WAVE the unit count is a multiple of 8, so whole waves leave;
-    // otherwise whole 8-lane groups.
-    if (unit >= total_units) return;
-    uint32_t rt;
-    if constexpr (ROW_WAVE)
-        rt = __builtin_amdgcn_readfirstlane(unit) >> log2H;  // the wave's (layer, row)
-    else
-        rt = unit >> log2H;
-    const uint32_t l = rt / rows;
-    const uint32_t t = rt - l * rows;
-
-    // The layers' operands, held in scalar registers and picked by compares
-    // (uniform with ROW_WAVE, per lane otherwise): indexing the argument
-    // arrays by l would be a memory load, one more round trip ahead of the
-    // row's own loads. The empty asm statements keep the compiler from
-    // folding the selection back into such a load.
+    uint32_t l, t, h;
     uint32_t l_rows = 0;
     uint64_t l_slots_a = 0, l_cache_a = 0;
+    if constexpr (ROW_WAVE) {
+        // Grid (row waves, layers): the layer is the block's y; the wave's
+        // first unit is a multiple of 8 <= H, so its 8 units are 8 heads of
+        // one row. The layer's operands come from the argument block at a
+        // uniform index (scalar loads).
+        l = blockIdx.y;
+        const uint32_t unit0 = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) >> 3 & ~7u);
+        t = unit0 >> log2H;
+        h = (unit0 & (H - 1u)) + ((threadIdx.x & 63u) >> 3);
+        l_rows = layers.rows[l];
+        l_slots_a = (uint64_t)(uintptr_t)layers.slots[l];
+        l_cache_a = (uint64_t)(uintptr_t)layers.cache[l];
+    } else {
+        const uint32_t unit = (blockIdx.x * blockDim.x + threadIdx.x) >> 3;
+        if (unit >= total_units) return;  // whole 8-lane groups leave together
+        h = unit & (H - 1u);
+        const uint32_t rt = unit >> log2H;
+        l = rt / rows;
+        t = rt - l * rows;
+        // The layers' operands, held in scalar registers and picked by
+        // compares: indexing the argument arrays by a per-lane l would be a
+        // memory load, one more round trip ahead of the row's own loads. The
+        // empty asm statements keep the compiler from folding the selection
+        // back into such a load.
 #pragma unroll
-    for (uint32_t i = 0; i < (uint32_t)kMaxLayersPerLaunch; ++i) {
-        uint32_t ri = layers.rows[i];
-        uint64_t si = (uint64_t)(uintptr_t)layers.slots[i];
-        uint64_t ci = (uint64_t)(uintptr_t)layers.cache[i];
-        asm volatile("" : "+s"(ri), "+s"(si), "+s"(ci));
-        if (l == i) {
-            l_rows = ri;
-            l_slots_a = si;
-            l_cache_a = ci;
+        for (uint32_t i = 0; i < (uint32_t)kMaxLayersPerLaunch; ++i) {
+            uint32_t ri = layers.rows[i];
+            uint64_t si = (uint64_t)(uintptr_t)layers.slots[i];
+            uint64_t ci = (uint64_t)(uintptr_t)layers.cache[i];
+            asm volatile("" : "+s"(ri), "+s"(si), "+s"(ci));
+            if (l == i) {
+                l_rows = ri;
+                l_slots_a = si;
+                l_cache_a = ci;
+            }
         }
     }
     if (t >= l_rows) return;  // past this layer's slot list (or a layer without one)
@@ -189,11 +198,18 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restric
 template <bool ROPE>
 void launch_rope(const KvStoreArgs& a, uint32_t total_units, hipStream_t stream) {
     const uint32_t threads = 256;
-    const uint32_t blocks = (uint32_t)(((uint64_t)total_units * 8 + threads - 1) / threads);
+    dim3 grid;
+    if (a.H >= 8) {
+        // one wave per 8 heads of a row: rows * H / 8 waves per layer, 4 per block
+        const uint64_t waves = (uint64_t)a.rows * a.H / 8;
+        grid = dim3((uint32_t)((waves + 3) / 4), a.layers_in_launch);
+    } else {
+        grid = dim3((uint32_t)(((uint64_t)total_units * 8 + threads - 1) / threads));
+    }
     auto kernel = a.H >= 8 ? kv_store_kernel<ROPE, true> : kv_store_kernel<ROPE, false>;
-    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(threads), 0, stream, a.k, a.v, a.k_ls, a.k_rs, a.v_ls, a.v_rs,
-                       a.positions, a.cos_sin, a.max_position, a.layers, a.rows, a.H, a.log2H, total_units,
-                       a.block_size, a.bs_shift, a.n_slots, a.block_stride, a.page_stride, a.head_stride, a.eps);
+    hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, a.k, a.v, a.k_ls, a.k_rs, a.v_ls, a.v_rs, a.positions,
+                       a.cos_sin, a.max_position, a.layers, a.rows, a.H, a.log2H, total_units, a.block_size,
+                       a.bs_shift, a.n_slots, a.block_stride, a.page_stride, a.head_stride, a.eps);
 }
 
 int launch_kv_store(const KvStoreArgs& a, hipStream_t stream) {
