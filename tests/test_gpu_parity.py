@@ -857,6 +857,45 @@ def test_store_skips_out_of_range_rows(nrc, oracle):
     assert_bits_equal(to_host(cd), want, "store with out-of-range rows")
 
 
+
+@pytest.mark.parametrize("H", [8, 2])
+@pytest.mark.parametrize("eps", [0.0, 1e-6])
+def test_store_non_finite_norm_and_rope(nrc, oracle, H, eps):
+    """Heads whose K-norm or RoPE meets zero, overflow, Inf and NaN: an
+    all-zero head (with eps = 0 its scale is infinite and 0 * inf = NaN), a
+    head whose sum of squares overflows (scale 0), heads holding one Inf or
+    one NaN, a head of subnormals, and cos/sin rows holding Inf and NaN. Both
+    grid forms (H >= 8: one row per wave; H < 8: per-lane rows)."""
+    from norm_rope_cache_amd import synth
+
+    L, T, bs, nb = 2, 48, 16, 8
+    N = 2 * H * 64
+    kv = synth.normal_bf16(8101 + H, (L, T, N), std=1.8)
+    kv[:, 1, 0:64] = 0                       # zero K head
+    kv[:, 2, 0:64] = 0x7F70                  # sum of squares overflows
+    kv[:, 3, 64 * (H - 1) + 5] = 0x7F80      # one +Inf in the last K head
+    kv[:, 4, 7] = 0xFFC1                     # one NaN
+    kv[:, 5, 0:64] = 0x0003                  # subnormals
+    kv[:, 6, 0:64] = 0x8000                  # -0 head
+    rng = np.random.default_rng(11)
+    slots = np.stack([rng.permutation(nb * bs)[:T] for _ in range(L)]).astype(np.int64)
+    positions = np.arange(T, dtype=np.int64) % 20
+    tab = synth.rope_table(20)
+    tab[9, 3] = 0x7F80                       # cos = +Inf
+    tab[10, 32 + 5] = 0x7FC3                 # sin = NaN
+    tab[11, :] = 0                           # cos = sin = 0
+    positions[12] = 9
+    positions[13] = 10
+    positions[14] = 11
+    positions[1] = 9                         # the zero head meets the Inf cos
+    caches = synth.random_bits_u16(8103, (L, nb, H, bs, 128))
+    _say(f"store non-finite H={H} eps={eps}")
+    cd = to_dev(caches)
+    nrc.context_kv_store(to_dev(kv), to_dev(positions), to_dev(slots), to_dev(tab), cd, H, eps)
+    want = caches.copy()
+    oracle.context_kv_store(kv, H, positions, slots, tab, want, bs, eps)
+    assert_bits_equal(to_host(cd), want, f"store non-finite H={H} eps={eps}")
+
 # --------------------------------------------------------------------- chain
 
 @pytest.mark.parametrize("fused", [False, True])
