@@ -10,10 +10,11 @@
 // with fully coalesced 128-byte runs and the fold's three cross-lane strides
 // are DPP / swizzle exchanges inside each 8-lane group.
 //
-// Work unit u = (layer, row, head) with the head fastest, taken by an
-// 8-lane group (lanes 8u .. 8u+7). Rows whose slot is negative (or out of
-// range, or whose position is out of range), and rows past their layer's
-// slot list, read nothing but their slot and position and write nothing.
+// Work unit = (layer, row, head), taken by an 8-lane group; heads are
+// fastest, then rows (then layers, in the H < 8 form's one-dimensional
+// grid). Rows whose slot is negative (or out of range, or whose position is
+// out of range), and rows past their layer's slot list, read nothing but
+// their slot and position and write nothing.
 // The cache is a strided view: (block, page, head) at block * block_stride +
 // page * page_stride + head * head_stride, K in the first 64 elements of the
 // 128-element run and V in the next 64.
@@ -120,10 +121,10 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restric
     uint32_t l_rows = 0;
     uint64_t l_slots_a = 0, l_cache_a = 0;
     if constexpr (ROW_WAVE) {
-        // Grid (row waves, layers): the layer is the block's y; the wave's
-        // first unit is a multiple of 8 <= H, so its 8 units are 8 heads of
-        // one row. The layer's operands come from the argument block at a
-        // uniform index (scalar loads).
+        // Grid (row waves, layers): the layer is the block's y. The wave's
+        // first unit is a multiple of 8 and H a power of two >= 8, so its 8
+        // units are 8 heads of one row. The layer's operands come from the
+        // argument block at a uniform index (scalar loads).
         l = blockIdx.y;
         const uint32_t unit0 = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) >> 3 & ~7u);
         t = unit0 >> log2H;
@@ -156,7 +157,9 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restric
             }
         }
     }
-    if (t >= l_rows) return;  // past this layer's slot list (or a layer without one)
+    // Past this layer's slot list, a layer without one, or (row waves) past
+    // the grid's last row: nothing to do.
+    if (t >= l_rows) return;
     // The slot and the position (every row below rows has one) in one round
     // trip, tested together; K, V and the cos/sin row in a second.
     const int64_t slot = ((const GlobalI64*)l_slots_a)[t];  // a device allocation: global memory
