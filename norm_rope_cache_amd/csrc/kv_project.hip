@@ -97,9 +97,12 @@ struct FusedA {
     float center;
 };
 
-// FUSED: false - A is the stacked layer-norm output [L, M, K] (tiles ordered
-// layer, M tile, N tile); true - A is built from FusedA (tiles ordered M
-// tile, layer, N tile, so the layers of one h panel run together).
+// Tiles are ordered layer, M tile, N tile (N fastest), so each XCD's share
+// of a round touches one layer's weight panels. FUSED: false - A is the
+// stacked layer-norm output [L, M, K]; true - A is built from FusedA (each h
+// panel is then read once per layer: ordering the layers of an h panel
+// together instead re-read the weight panels of every layer in each round,
+// 2.6 GB fetched per launch, and ran 2% slower).
 // CMODE (fused, with weights): 0 - gamma = w; 1 - gamma = w with -0.0 turned
 // into +0.0 (a +0.0 center); 2 - gamma = w + center in FP32.
 // B_ND: the weight is stored [L, N, K] (K contiguous, the pages' storage)
@@ -149,16 +152,10 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     const int64_t k_len = SPLIT ? K / k_split : K;  // K walked per tile
     auto decode = [&](int tile) {
         const int tn = tile % tiles_n;
-        int tm;
-        if constexpr (FUSED) {
-            layer = (tile / tiles_n) % L;
-            tm = tile / (tiles_n * L);
-        } else {
-            tm = (tile / tiles_n) % tiles_m;
-            const int lt = tile / (tiles_n * tiles_m);
-            layer = SPLIT ? lt % L : lt;
-            ks = SPLIT ? lt / L : 0;
-        }
+        const int tm = (tile / tiles_n) % tiles_m;
+        const int lt = tile / (tiles_n * tiles_m);
+        layer = SPLIT ? lt % L : lt;
+        ks = SPLIT ? lt / L : 0;
         m0 = (int64_t)tm * BM;
         n0 = (int64_t)tn * BN;
     };
