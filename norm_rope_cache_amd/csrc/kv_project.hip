@@ -7,20 +7,23 @@
 //
 // Kernel: one workgroup per BM x BN output tile of one layer; waves split
 // the tile WM x WN, each wave owning a (BM/WM) x (BN/WN) block of
-// v_mfma_f32_32x32x16_bf16 accumulators. K is walked in stages of 32 through
-// a 4-deep LDS ring:
+// v_mfma_f32_16x16x32_bf16 accumulators (one MFMA per 16 x 16 block covers a
+// whole 32-wide stage of K). On this chip the 16 x 16 x 32 form draws less
+// power per flop than 32 x 32 x 16 (a loop of either on toggling operands
+// holds 1.95 against 1.75 GHz) and accumulates in the same order (identical
+// bits). K is walked in stages of 32 through a 4-deep LDS ring:
 //   - both operands go global -> LDS with global_load_lds_dwordx4 (no
 //     register staging); A rows are 64 bytes per stage, B k-rows 2 BN bytes;
 //   - A fragments are read with ds_read_b128 (8 consecutive k of one row),
 //     B fragments with ds_read_b64_tr_b16, which transposes the N-contiguous
 //     B tile into the k-contiguous operand layout on the fly;
 //   - XOR swizzles on 16-byte chunks (A: chunk ^ ((row >> 2) & 3), B: chunk
-//     ^ 4 (k-row & 3)) make every fragment read cover all 64 LDS banks;
-//   - each stage is two k16 sub-steps; the loop is scheduled by hand (one
-//     LDS read or DMA between consecutive MFMAs, sched_barrier fences) so
-//     the next sub-step's fragments and the DMA of the stage four ahead are
-//     in flight while the matrix core works, with DMA issue spread over the
-//     whole stage;
+//     ^ (4 (k-row & 3) ^ ((k-row >> 3) & 3))) spread every fragment read over
+//     the 64 LDS banks;
+//   - the loop is scheduled by hand (reads and DMA between consecutive
+//     MFMAs, sched_barrier fences): while stage st is multiplied, the
+//     fragments of stage st + 1 are read and the DMA of stage st + 3 goes
+//     out, one barrier per stage;
 //   - consecutive tile ids go to one XCD (workgroup ids are dealt
 //     round-robin over the 8 XCDs), so tiles sharing an A panel or a B panel
 //     meet in one L2.
@@ -35,7 +38,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4v lds_u32x4;
@@ -45,15 +48,15 @@ constexpr int kStages = 4;  // LDS ring depth
 
 // 16-byte chunk swizzles of the LDS tiles (see the header).
 __device__ __forceinline__ int swz_a(int row) { return (row >> 2) & 3; }
-__device__ __forceinline__ int swz_b(int krow) { return 4 * (krow & 3); }
+__device__ __forceinline__ int swz_b(int krow) { return (4 * (krow & 3)) ^ ((krow >> 3) & 3); }
 
 template <int BM, int BN, int WM, int WN>
 struct Cfg {
     static constexpr int WAVES = WM * WN;              // waves per workgroup, WM along M x WN along N
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int WTM = BM / WM, WTN = BN / WN; // wave tile
-    static constexpr int MI = WTM / 32;                // 32-row MFMA blocks per wave
-    static constexpr int NI = WTN / 32;                // 32-column MFMA blocks per wave
+    static constexpr int MI = WTM / 16;                // 16-row MFMA blocks per wave
+    static constexpr int NI = WTN / 16;                // 16-column MFMA blocks per wave
     static constexpr int A_BYTES = BM * kBK * 2;       // one stage of A: BM rows x 64 bytes
     static constexpr int B_BYTES = kBK * BN * 2;       // one stage of B: 32 k rows x 2 BN bytes
     static constexpr int B_ROW = BN * 2;
@@ -272,76 +275,64 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
         }
     };
 
-    // ---- MFMA operand reads.
-    // A (ds_read_b128): lane reads row wm BM/2 + 32 i + (lane & 31), k chunk
-    // 2 kk + (lane >> 5) of the 32-wide stage.
-    const int khalf = lane >> 5;
-    int a_off[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        const int r = wm * CF::WTM + (lane & 31);
-        a_off[kk] = r * 64 + 16 * ((2 * kk + khalf) ^ swz_a(r));
+    // ---- MFMA operand reads (v_mfma_f32_16x16x32_bf16: lane l supplies row
+    // (or column) l % 16 of its 16-block and the 8 k values 8 (l / 16) ..
+    // 8 (l / 16) + 7 of the 32-wide stage; one MFMA covers a whole stage).
+    // A (ds_read_b128): lane reads row wm WTM + 16 i + (lane & 15), k chunk
+    // lane >> 4; block i adds 16 rows (1 KiB; the swizzle repeats every 4 rows).
+    const int kq = lane >> 4;
+    int a_off;
+    {
+        const int r = wm * CF::WTM + (lane & 15);
+        a_off = r * 64 + 16 * (kq ^ swz_a(r));
     }
-    // B (ds_read_b64_tr_b16): within each 16-lane group g, lane c = 4 jj + q
-    // points at 4 bf16 of k row kbase + jj, columns 4 q .. 4 q + 3 of the
-    // group's 16 columns; the transposing read hands lane i of the group the
-    // 4 k values kbase .. kbase + 3 of column i. Groups 0/1 cover columns
-    // 0-15/16-31 of the block at k 0..7 of the sub-step, groups 2/3 k 8..15.
+    // B (ds_read_b64_tr_b16): within each 16-lane group g = lane >> 4, lane
+    // c = 4 jj + q points at 4 bf16 of k row 8 g + 4 h + jj, columns 4 q ..
+    // 4 q + 3 of the block's 16 columns; the transposing read hands lane i of
+    // the group the 4 k values 8 g + 4 h .. 8 g + 4 h + 3 of column i, which
+    // are elements 4 h .. 4 h + 3 of its operand. Half h = 1 is 4 k rows on.
     int b_off[CF::NI];
     {
-        const int g = lane >> 4, c = lane & 15, jj = c >> 2, q = c & 3;
-        const int krow = 8 * (g >> 1) + jj;
+        const int c = lane & 15, jj = c >> 2, q = c & 3;
+        const int krow = 8 * kq + jj;
 #pragma unroll
         for (int j = 0; j < CF::NI; ++j) {
-            const int n = wn * CF::WTN + 32 * j + 16 * (g & 1) + 4 * q;
-            const int pc = (n >> 3) ^ swz_b(jj);
+            const int n = wn * CF::WTN + 16 * j + 4 * q;
+            const int pc = (n >> 3) ^ swz_b(krow);
             b_off[j] = CF::A_REGION + krow * CF::B_ROW + pc * 16 + ((n >> 2) & 1) * 8;
         }
     }
+    // B stored [L, N, K]: lane reads column row wn WTN + 16 j + (lane & 15),
+    // k chunk lane >> 4, as for A.
+    int bnd_off;
+    {
+        const int r = wn * CF::WTN + (lane & 15);
+        bnd_off = CF::A_REGION + r * 64 + 16 * (kq ^ swz_a(r));
+    }
 
-    // B stored [L, N, K]: lane reads column row wn BN/WN + 32 j + (lane & 31),
-    // k chunk 2 kk + (lane >> 5), as for A.
-    int bnd_off[2][CF::NI];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int j = 0; j < CF::NI; ++j) {
-            const int r = wn * CF::WTN + 32 * j + (lane & 31);
-            bnd_off[kk][j] = CF::A_REGION + r * 64 + 16 * ((2 * kk + khalf) ^ swz_a(r));
-        }
-
-    f32x16 acc[CF::MI][CF::NI];
+    f32x4 acc[CF::MI][CF::NI];
 
     // ---- one-instruction building blocks of the scheduled loop.
-    // Fragment set f holds one k16 sub-step: af[f][i] for the wave's 32-row
-    // blocks i, bfr[f][j] for its 32-column blocks j.
-    bf16x8 af[2][CF::MI], bfr[2][CF::NI];
-    constexpr int NM = CF::MI * CF::NI;      // MFMAs per sub-step
-    constexpr int NR = CF::MI + (B_ND ? 1 : 2) * CF::NI;  // LDS reads per sub-step
-    constexpr int HALF = CF::LOADS / 2;      // DMAs issued per sub-step
-    static_assert(CF::LOADS % 2 == 0 && HALF <= NM, "DMA spread");
-    // LDS read r of sub-step (buf, kk) into set f, in the order the MFMAs
-    // consume them: A0, B0 (two transposing halves, or one read for the
-    // [L, N, K] storage), B1, ..., then A1, A2, ..
-    auto read_one = [&](int buf, int kk, int f, int r) {
+    // af[i] holds the wave's 16-row block i of a stage; bfr[f][j] its
+    // 16-column block j, in two sets (f = stage parity): the next stage's B
+    // blocks are read while the current ones are still in use, and each A
+    // block of the next stage is read into af[i] once block i's last MFMA
+    // has issued.
+    bf16x8 af[CF::MI], bfr[2][CF::NI];
+    constexpr int NM = CF::MI * CF::NI;                 // MFMAs per stage
+    constexpr int NB = (B_ND ? 1 : 2) * CF::NI;          // B reads per stage
+    auto read_a = [&](int buf, int i) {
+        af[i] = *(const __attribute__((address_space(3))) bf16x8*)(lds + buf * CF::A_BYTES + a_off + i * 16 * 64);
+    };
+    // B read r (0 .. NB - 1) of stage buffer buf into set f.
+    auto read_b = [&](int buf, int f, int r) {
         typedef short i16x8 __attribute__((ext_vector_type(8)));
-        const lds_char* sa = lds + buf * CF::A_BYTES;
         const lds_char* sb = lds + buf * CF::B_BYTES;
         if constexpr (B_ND) {
-            if (r == 0 || r > CF::NI) {
-                const int i = r == 0 ? 0 : r - CF::NI;
-                af[f][i] = *(const __attribute__((address_space(3))) bf16x8*)(sa + a_off[kk] + i * 32 * 64);
-            } else {
-                bfr[f][r - 1] = *(const __attribute__((address_space(3))) bf16x8*)(sb + bnd_off[kk][r - 1]);
-            }
-            return;
-        }
-        if (r == 0 || r > 2 * CF::NI) {
-            const int i = r == 0 ? 0 : r - 2 * CF::NI;
-            af[f][i] = *(const __attribute__((address_space(3))) bf16x8*)(sa + a_off[kk] + i * 32 * 64);
+            bfr[f][r] = *(const __attribute__((address_space(3))) bf16x8*)(sb + bnd_off + r * 16 * 64);
         } else {
-            const int j = (r - 1) >> 1, hi = (r - 1) & 1;
-            const lds_char* p = sb + b_off[j] + kk * 16 * CF::B_ROW + hi * 4 * CF::B_ROW;
+            const int j = r >> 1, hi = r & 1;
+            const lds_char* p = sb + b_off[j] + hi * 4 * CF::B_ROW;
             const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
             const i16x8 v8 = __builtin_shufflevector(v, v, 0, 1, 2, 3, 0, 1, 2, 3);
             const i16x8 cur = __builtin_bit_cast(i16x8, bfr[f][j]);
@@ -352,7 +343,7 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     };
     auto mfma_one = [&](int f, int idx) {
         const int i = idx / CF::NI, j = idx % CF::NI;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f][i], bfr[f][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[f][j], acc[i][j], 0, 0, 0);
     };
     const int nk = (int)(k_len / kBK);
     // DMA d (0 .. LOADS-1: A blocks, then B blocks) of stage st into buffer
@@ -374,32 +365,28 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
         }
     };
 
-    // ---- pipeline. Iteration st (stage st in buffer b = st mod 4, its
-    // first sub-step's fragments already in set 0):
-    //   sub-step 0: MFMAs on set 0; between them the reads of set 1 (stage
-    //               st, second sub-step) and the second half of stage
-    //               st + 3's DMA;
-    //   wait until stage st + 1 has landed (own DMAs; the fused form waits
-    //   at the top instead and rebuilds its A chunks during sub-step 0),
-    //   then wait for this wave's LDS traffic and barrier (stage st + 1
-    //   visible to all, buffer b free);
-    //   sub-step 1: MFMAs on set 1; between them the first half of stage
-    //               st + 4's DMA (into buffer b) and the reads of set 0 of
-    //               stage st + 1.
-    // DMA issue order is stage by stage, so "stage st + 1 landed" is
-    // vmcnt <= the loads of stages st + 2 and st + 3 = 2 LOADS.
-    // ---- tiles. The first tile's setup and prologue DMA (stages 0-2 and
-    // the first half of stage 3) go out before the loop; each later tile's
-    // go out as soon as the previous tile's K loop has finished, before that
-    // tile's results are stored, so the store burst and the first loads of
-    // the next tile overlap.
+    // ---- pipeline. Stage st is computed from fragments read during stage
+    // st - 1. Iteration st:
+    //   wait until this wave's DMAs of stage st + 1 have landed (vmcnt <= the
+    //   loads of stage st + 2, the only later ones issued), barrier: stage
+    //   st + 1 visible to all;
+    //   the NM MFMAs of stage st (A block by A block); between them the DMA
+    //   of stage st + 3 into buffer (st + 3) mod 4 = (st - 1) mod 4, whose
+    //   fragments were read during stage st - 2 and used before this
+    //   iteration's barrier, and the reads of stage st + 1: its B blocks into
+    //   the other B set, and each A block into af[i] after block i's last
+    //   MFMA. The fused form first rebuilds this lane's A chunks of stage
+    //   st + 1 between the first half's MFMAs and takes a second barrier
+    //   before any read of that stage; its reads go in the second half.
+    // ---- tiles. The first tile's setup and prologue DMA (stages 0-2) go out
+    // before the loop; each later tile's go out as soon as the previous
+    // tile's K loop has finished, before that tile's results are stored, so
+    // the store burst and the first loads of the next tile overlap.
     auto issue_prologue = [&]() {
 #pragma unroll
         for (int st = 0; st < kStages - 1; ++st)
 #pragma unroll
             for (int d = 0; d < CF::LOADS; ++d) dma_one(st, d);
-#pragma unroll
-        for (int d = 0; d < HALF; ++d) dma_one(kStages - 1, d);
     };
     int it = 0;
     int tile = tile_of(0);
@@ -408,8 +395,8 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     set_sources();
     set_fused();
     issue_prologue();
-    // Epilogue: lane holds column (lane & 31) of each 32 x 32 block, rows
-    // 8 (v / 4) + 4 (lane / 32) + (v % 4).
+    // Epilogue: lane holds column (lane & 15) of each 16 x 16 block, rows
+    // 4 (lane / 16) + v, v < 4.
     auto epilogue = [&](int e_layer, int64_t e_m0, int64_t e_n0, int e_ks) {
     uint16_t* Cl = C + (int64_t)e_layer * M * N;
     float* Wl = W + ((int64_t)e_ks * L + e_layer) * M * N;
@@ -418,10 +405,10 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
         for (int i = 0; i < CF::MI; ++i)
 #pragma unroll
             for (int j = 0; j < CF::NI; ++j) {
-                const int64_t col = e_n0 + wn * CF::WTN + 32 * j + (lane & 31);
+                const int64_t col = e_n0 + wn * CF::WTN + 16 * j + (lane & 15);
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int64_t row = e_m0 + wm * CF::WTM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                for (int v = 0; v < 4; ++v) {
+                    const int64_t row = e_m0 + wm * CF::WTM + 16 * i + 4 * (lane >> 4) + v;
                     if (decltype(checked)::value && row >= M) continue;
                     if constexpr (SPLIT)
                         Wl[row * N + col] = acc[i][j][v];
@@ -436,72 +423,86 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
         store_tile(std::true_type{});
     };
 
+    // Slots of the schedule (MFMA index after which a piece is issued).
+    constexpr int HALFM = NM / 2;
+    auto dma_slot = [](int d) { return (d * NM) / CF::LOADS + 1 < NM ? (d * NM) / CF::LOADS + 1 : NM - 1; };
+    // unfused: B reads spread over the first NB slots; fused: over the second half
+    auto b_slot = [](int r) { return FUSED ? HALFM + (r * HALFM) / NB : (r * NM) / (2 * NB); };
+    // A block i of the next stage: after its last MFMA (fused: not before the half)
+    auto a_slot = [](int i) {
+        const int last = i * CF::NI + CF::NI - 1;
+        return FUSED && last < HALFM ? HALFM + i : last;
+    };
+    constexpr int NP = 4 * CF::A_LOADS;  // fused: element pairs per lane per stage
+    auto pair_slot = [](int p) { return HALFM > 1 ? 1 + (p * (HALFM - 1)) / NP : 0; };
+
     while (true) {
 #pragma unroll
         for (int i = 0; i < CF::MI; ++i)
 #pragma unroll
             for (int j = 0; j < CF::NI; ++j)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-        // Stage 0 landed. On the first tile: vmcnt <= stages 1-2 and half of
-        // 3; later tiles also have the previous tile's stores in flight,
-        // issued after these loads, so wait for everything.
+                for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0f;
+        // Stage 0 landed. On the first tile: vmcnt <= stages 1-2; later tiles
+        // also have the previous tile's stores in flight, issued after these
+        // loads, so wait for everything.
         if (it == 0)
-            wait_vmcnt<(kStages - 2) * CF::LOADS + HALF>();
+            wait_vmcnt<(kStages - 2) * CF::LOADS>();
         else
             wait_vmcnt<0>();
-        if constexpr (FUSED) __syncthreads();  // staged weights visible to every wave
         if constexpr (FUSED) {
+            __syncthreads();  // staged weights visible to every wave
             transform(0, 0);
             wait_lgkmcnt0();
         }
         barrier();
 #pragma unroll
-        for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
-        // Fused form: the A chunks of stage st + 1 are rebuilt during sub-step
-        // 0, so that stage is waited for at the top of the iteration (vmcnt <=
-        // stage st + 2 and the first half of st + 3); its reads go in the first
-        // slot, its element pairs over the remaining slots, each chunk written
-        // back after its last pair.
-        constexpr int NP = 4 * CF::A_LOADS;  // element pairs per lane per stage
-        auto pair_slot = [](int p) { return NM > 1 ? 1 + (p * (NM - 1)) / NP : 0; };
-        for (int st = 0; st < nk; ++st) {
-            const int b = st & (kStages - 1);
+        for (int i = 0; i < CF::MI; ++i) {
+            read_a(0, i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int r = 0; r < NB; ++r) {
+            read_b(0, 0, r);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Two iterations per loop trip (nk is even): B sets 0 then 1.
+        auto iteration = [&](int st, auto fset) {
+            constexpr int f = decltype(fset)::value;
             const int b1 = (st + 1) & (kStages - 1);
-            if constexpr (FUSED) wait_vmcnt<CF::LOADS + HALF>();
+            wait_vmcnt<CF::LOADS>();
+            barrier();
+            if constexpr (FUSED) t_read(st + 1, b1);
 #pragma unroll
             for (int idx = 0; idx < NM; ++idx) {
-                mfma_one(0, idx);
+                mfma_one(f, idx);
                 if constexpr (FUSED) {
-                    if (idx == 0) t_read(st + 1, b1);
 #pragma unroll
                     for (int p = 0; p < NP; ++p)
-                        if (pair_slot(p) == idx) {
+                        if (idx < HALFM && pair_slot(p) == idx) {
                             t_pair(p >> 2, p & 3);
                             if ((p & 3) == 3) t_write(b1, p >> 2);
                         }
+                    if (idx == HALFM - 1) {
+                        wait_lgkmcnt0();
+                        barrier();  // every wave's rebuilt chunks of stage st + 1 visible
+                    }
                 }
 #pragma unroll
-                for (int r = (idx * NR) / NM; r < ((idx + 1) * NR) / NM; ++r) read_one(b, 1, 1, r);
+                for (int d = 0; d < CF::LOADS; ++d)
+                    if (dma_slot(d) == idx) dma_one(st + kStages - 1, d);
 #pragma unroll
-                for (int d = 0; d < HALF; ++d)
-                    if (idx == ((d * NM) / HALF + 2 < NM ? (d * NM) / HALF + 2 : NM - 1))
-                        dma_one(st + kStages - 1, HALF + d);
+                for (int r = 0; r < NB; ++r)
+                    if (b_slot(r) == idx) read_b(b1, f ^ 1, r);
+#pragma unroll
+                for (int i = 0; i < CF::MI; ++i)
+                    if (a_slot(i) == idx) read_a(b1, i);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (!FUSED) wait_vmcnt<(kStages - 2) * CF::LOADS>();
-            wait_lgkmcnt0();
-            barrier();
-#pragma unroll
-            for (int idx = 0; idx < NM; ++idx) {
-                mfma_one(1, idx);
-#pragma unroll
-                for (int d = 0; d < HALF; ++d)
-                    if (idx == ((d * NM) / HALF + 1 < NM ? (d * NM) / HALF + 1 : NM - 1)) dma_one(st + kStages, d);
-#pragma unroll
-                for (int r = (idx * NR) / NM; r < ((idx + 1) * NR) / NM; ++r) read_one(b1, 0, 0, r);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        };
+        for (int st = 0; st < nk; st += 2) {
+            iteration(st, std::integral_constant<int, 0>{});
+            iteration(st + 1, std::integral_constant<int, 1>{});
         }
         wait_vmcnt<0>();  // the clamped loads past the last stage have landed
         barrier();         // every wave is done with the ring and the weights
