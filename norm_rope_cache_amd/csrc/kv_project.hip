@@ -535,6 +535,10 @@ int launch_tiles(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
     const int tiles_m = (int)((a.M + BM - 1) / BM);
     const int tiles_n = (int)(a.N / BN);
     const int total = a.L * tiles_m * tiles_n * (SPLIT ? a.k_split : 1);
+    // The K loop takes two 32-wide stages per trip: every workgroup's share
+    // of K must be a multiple of 64 (the callers' shapes and the split rule
+    // guarantee it; anything else is refused rather than summed wrong).
+    if ((a.K / (SPLIT ? a.k_split : 1)) % (2 * kBK) != 0 || (SPLIT && a.K % a.k_split != 0)) return -1;
     const size_t lds_bytes = CF::LDS_BYTES + ((FUSED && PW) ? (size_t)a.K * 2 : 0);
     auto kernel = kv_project_kernel<BM, BN, WM, WN, FUSED, PW, CMODE, B_ND, SPLIT>;
     if (lds_bytes > 65536) {
@@ -610,14 +614,14 @@ int32_t kv_project_k_split(int32_t L, int64_t M, int64_t K, int64_t N, int num_c
     if (N % 256 == 0 && big_tiles >= cus) return 1;
     // Slices of 256 x 256 tiles (N a multiple of 256, at least 256 rows) up
     // to one per CU, else of 128 x 128 tiles up to two per CU (their LDS ring
-    // lets two share a CU); at most 8 slices, each a whole number of at least
-    // 4 stages.
+    // lets two share a CU); at most 8 slices, each an even number (the loop
+    // takes two stages per trip) of at least 4 stages.
     const bool big = N % 256 == 0 && M >= 256;
     const int64_t tiles = big ? big_tiles : (int64_t)L * ((M + 127) / 128) * (N / 128);
     const int64_t target = big ? (int64_t)cus : 2 * (int64_t)cus;
     const int64_t nk = K / kBK;
     int32_t s = 1;
-    while (tiles * s < target && s < 8 && nk % (2 * s) == 0 && nk / (2 * s) >= 4) s *= 2;
+    while (tiles * s < target && s < 8 && nk % (4 * s) == 0 && nk / (2 * s) >= 4) s *= 2;
     return s;
 }
 

@@ -589,6 +589,31 @@ def test_project_timed_matches_and_stamps(nrc, L, T, N):
     z, clk0 = nrc.context_kv_project_timed(A[:, :0], B)
     assert clk0["workgroups"] == 0 and z.shape == (L, 0, N)
 
+
+@pytest.mark.parametrize("D", [192, 320, 640, 1088])
+@pytest.mark.parametrize("T", [40, 1300])
+def test_project_other_summation_lengths(nrc, oracle, D, T):
+    """Summation lengths other than 8192 (any multiple of 64): the one-pass
+    and split forms (few rows split D when the split rule allows an even
+    number of 32-wide stages per slice) and both weight layouts, within
+    tolerance of the oracle; the two layouts give the same bits."""
+    from norm_rope_cache_amd import synth
+
+    L, N = 2, 256
+    A = synth.normal_bf16(4500 + D, (L, T, D))
+    B = synth.normal_bf16(4600 + D, (L, D, N), std=0.02)
+    Ad, Bd = to_dev(A), to_dev(B)
+    _say(f"project D={D} T={T}")
+    Cstar = oracle.kv_project(A, B)
+    outs = {}
+    for split in (False, True):
+        c = to_host(nrc.context_kv_project(Ad, Bd, split=split))
+        ok, msg = projection_tolerance_ok(c, Cstar)
+        assert ok, f"D={D} T={T} split={split}: {msg}"
+        outs[split] = c
+    c_nd = to_host(nrc.context_kv_project(Ad, to_dev(np.ascontiguousarray(np.swapaxes(B, 1, 2))), w_layout="nd"))
+    assert_bits_equal(c_nd, outs[True], f"[L, N, D] vs [L, D, N] D={D} T={T}")
+
 @pytest.mark.parametrize("L,T,N", [(4, 3000, 1024), (2, 4196, 2048), (1, 8292, 2560)])
 def test_project_several_tiles_per_workgroup(nrc, oracle, L, T, N):
     """Shapes with more output tiles than resident workgroups, so each
