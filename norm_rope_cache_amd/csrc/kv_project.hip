@@ -471,7 +471,13 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
             constexpr int f = decltype(fset)::value;
             const int b1 = (st + 1) & (kStages - 1);
             wait_vmcnt<CF::LOADS>();
-            barrier();
+            // The fused form's only barrier is the mid-stage one: its rebuilt
+            // chunks are read only after it, and no wave can issue the DMA
+            // into buffer (st - 1) mod 4 before every wave has passed the
+            // previous stage's mid barrier, by which point their reads of
+            // that buffer (stage st - 1, read during stage st - 2) were
+            // consumed.
+            if constexpr (!FUSED) barrier();
             if constexpr (FUSED) t_read(st + 1, b1);
 #pragma unroll
             for (int idx = 0; idx < NM; ++idx) {
