@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kBlockThreads) void context_norms_kernel(
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ float sums[kSlots][2][4];
     const int tid = threadIdx.x;
-    const int slot = tid >> 8;
+    const int slot = __builtin_amdgcn_readfirstlane(tid >> 8);  // a slot is four whole waves
     const int t = tid & (kThreads - 1);
     const int col0 = 8 * t;
     const bool fix_h = !ADD_CENTER && !__builtin_signbit(hidden_center);
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(kBlockThreads) void context_norms_kernel(
             for (int i = 0; i < 8; ++i) u[k][i] = u[k][i] * rp;
 
         auto layer_out = [&](int l, auto fast) {
-            uint16_t* o = out + ((int64_t)l * T + row) * kHidden + col0;
+            const uint16_t* orow = out + ((int64_t)l * T + row) * kHidden;  // the same in every lane of the wave
 #pragma unroll
             for (int k = 0; k < kFrags; ++k) {
                 uint32_t w[4];
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kBlockThreads) void context_norms_kernel(
                     }
                     w[p] = decltype(fast)::value ? pack_bf16_fast(a, b) : pack_bf16(a, b);
                 }
-                store16_nt(o + k * kChunk, U32x4{w[0], w[1], w[2], w[3]});
+                store16_stream(orow, kRowBytes, (uint32_t)(col0 + k * kChunk) * 2, U32x4{w[0], w[1], w[2], w[3]});
             }
         };
         if (active) {

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kBlockThreads) void draft_boundary_kernel(
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ float sums[kSlots][2][4];
     const int tid = threadIdx.x;
-    const int slot = tid >> 8;
+    const int slot = __builtin_amdgcn_readfirstlane(tid >> 8);  // a slot is four whole waves
     const int t = tid & (kThreads - 1);
     const int wv = t >> 6;
     const int lane = t & 63;
@@ -258,8 +258,9 @@ __global__ __launch_bounds__(kBlockThreads) void draft_boundary_kernel(
                 }
                 if constexpr (STORE) {
                     if (active)
-                        store16_nt(stream_out + rbase + c, U32x4{__float_as_uint(res[0]), __float_as_uint(res[1]),
-                                                                 __float_as_uint(res[2]), __float_as_uint(res[3])});
+                        store16_stream(stream_out + rbase, kHidden * 4, (uint32_t)c * 4,
+                                       U32x4{__float_as_uint(res[0]), __float_as_uint(res[1]),
+                                             __float_as_uint(res[2]), __float_as_uint(res[3])});
                 }
                 zw[h] = make_uint2(pack_bf16(res[0], res[1]), pack_bf16(res[2], res[3]));
             }
@@ -297,8 +298,9 @@ __global__ __launch_bounds__(kBlockThreads) void draft_boundary_kernel(
                     o[i] = u[k][i] * r2;
                     if (pre_w_on && !pre_in) o[i] = o[i] * gq[i];
                 }
-                store16_nt(out + rbase + col0 + k * kChunk, U32x4{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]),
-                                                                   pack_bf16(o[4], o[5]), pack_bf16(o[6], o[7])});
+                store16_stream(out + rbase, kHidden * 2, (uint32_t)(col0 + k * kChunk) * 2,
+                               U32x4{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]),
+                                     pack_bf16(o[6], o[7])});
             }
         }
     }

@@ -37,6 +37,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kFrags = 4;
+constexpr uint32_t kRowBytesOut = 8192 * 2;  // one bf16 output row
 constexpr int kChunk = 2048;  // kThreads * 8
 
 // Eight gamma values (w + center) of a weight row at column c (a multiple
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void norms_ex_kernel(const uint16_t* __re
                     for (int i = 0; i < 8; ++i) v[k][i] = g[k][i] * u[k][i];
                 rp = rsqrt_rn(__builtin_fmaf(row_sum(lane_sumsq(v)), 0x1p-13f, pre_eps));
             }
-            uint16_t* o = out + ((int64_t)l * T + row) * kHidden + col0;
+            const uint16_t* orow = out + ((int64_t)l * T + row) * kHidden;  // one row per workgroup
 #pragma unroll
             for (int k = 0; k < kFrags; ++k) {
                 float y[8];
@@ -161,8 +162,9 @@ __global__ __launch_bounds__(kThreads) void norms_ex_kernel(const uint16_t* __re
                         if constexpr (PK != 0) y[i] = y[i] * g[k][i];
                     }
                 }
-                store16_nt(o + k * kChunk, U32x4{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]),
-                                                 pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])});
+                store16_stream(orow, kRowBytesOut, (uint32_t)(col0 + k * kChunk) * 2,
+                               U32x4{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
+                                     pack_bf16(y[6], y[7])});
             }
         }
     }
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(kBlockThreads) void norms_ex_lds_kernel(
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ float sums[kSlots][1 + kMaxLdsLayers][4];
     const int tid = threadIdx.x;
-    const int slot = tid >> 8;
+    const int slot = __builtin_amdgcn_readfirstlane(tid >> 8);  // a slot is four whole waves
     const int t = tid & (kThreads - 1);
     const int wv = t >> 6;  // wave within the slot
     const int col0 = 8 * t;
@@ -341,7 +343,8 @@ __global__ __launch_bounds__(kBlockThreads) void norms_ex_lds_kernel(
             for (int p = 0; p < 4; ++p)
                 w[p] = decltype(fast)::value ? pack_bf16_pair_hw(y[2 * p], y[2 * p + 1])
                                              : pack_bf16(y[2 * p], y[2 * p + 1]);
-            store16_nt(out + ((int64_t)l * T + row) * kHidden + col0 + k * kChunk, U32x4{w[0], w[1], w[2], w[3]});
+            store16_stream(out + ((int64_t)l * T + row) * kHidden, kRowBytesOut, (uint32_t)(col0 + k * kChunk) * 2,
+                           U32x4{w[0], w[1], w[2], w[3]});
         };
         if (!per_layer) {
             // one layer-norm sum serves every layer: y = (u * rp) * gamma_l
