@@ -115,7 +115,8 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restric
                                                        StoreLayers layers, uint32_t rows, uint32_t H,
                                                        uint32_t log2H, uint32_t total_units, uint32_t block_size,
                                                        int32_t bs_shift, uint32_t n_slots, int64_t block_stride,
-                                                       int64_t page_stride, int64_t head_stride, float eps) {
+                                                       int64_t page_stride, int64_t head_stride, float eps,
+                                                       uint32_t head_span) {
     const uint32_t g = threadIdx.x & 7u;  // this lane's 8 elements of the head: 8g .. 8g+7
     uint32_t l, t, h;
     uint32_t l_rows = 0;
@@ -189,13 +190,23 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restric
         block = s32 / block_size;
         page = s32 - block * block_size;
     }
-    GlobalU16* dst = (GlobalU16*)l_cache_a + (int64_t)block * block_stride + (int64_t)page * page_stride +
-                     (int64_t)h * head_stride + 8 * g;
     // Non-temporal: the cache rows are scattered and not read back by this
     // chain, so they go out to HBM now instead of lingering dirty in the
-    // caches until the next kernel's traffic evicts them.
-    store16_nt_global(dst, out);
-    store16_nt_global(dst + kHeadDim, vw);
+    // caches until the next kernel's traffic evicts them. With one row per
+    // wave the (block, page) base is wave-uniform and the heads lie within
+    // head_span bytes of it (0: too far apart for a 32-bit offset), so the
+    // stores take the buffer form at system scope, which streams faster.
+    if (ROW_WAVE && head_span != 0) {
+        const uint16_t* base = (const uint16_t*)l_cache_a + (int64_t)block * block_stride + (int64_t)page * page_stride;
+        const uint32_t off = (uint32_t)((h * (uint64_t)head_stride + 8 * g) * 2);
+        store16_stream(base, head_span, off, out);
+        store16_stream(base, head_span, off + 2 * kHeadDim, vw);
+    } else {
+        GlobalU16* dst = (GlobalU16*)l_cache_a + (int64_t)block * block_stride + (int64_t)page * page_stride +
+                         (int64_t)h * head_stride + 8 * g;
+        store16_nt_global(dst, out);
+        store16_nt_global(dst + kHeadDim, vw);
+    }
 }
 
 template <bool ROPE>
@@ -210,9 +221,12 @@ void launch_rope(const KvStoreArgs& a, uint32_t total_units, hipStream_t stream)
         grid = dim3((uint32_t)(((uint64_t)total_units * 8 + threads - 1) / threads));
     }
     auto kernel = a.H >= 8 ? kv_store_kernel<ROPE, true> : kv_store_kernel<ROPE, false>;
+    // bytes from a row's (block, page) base to the end of its last head's run
+    const uint64_t span = ((uint64_t)(a.H - 1) * (uint64_t)a.head_stride + 2 * kHeadDim) * 2;
+    const uint32_t head_span = span < (1ull << 31) ? (uint32_t)span : 0u;
     hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, a.k, a.v, a.k_ls, a.k_rs, a.v_ls, a.v_rs, a.positions,
                        a.cos_sin, a.max_position, a.layers, a.rows, a.H, a.log2H, total_units, a.block_size,
-                       a.bs_shift, a.n_slots, a.block_stride, a.page_stride, a.head_stride, a.eps);
+                       a.bs_shift, a.n_slots, a.block_stride, a.page_stride, a.head_stride, a.eps, head_span);
 }
 
 int launch_kv_store(const KvStoreArgs& a, hipStream_t stream) {

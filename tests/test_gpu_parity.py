@@ -921,6 +921,42 @@ def test_store_non_finite_norm_and_rope(nrc, oracle, H, eps):
     oracle.context_kv_store(kv, H, positions, slots, tab, want, bs, eps)
     assert_bits_equal(to_host(cd), want, f"store non-finite H={H} eps={eps}")
 
+
+def test_store_ex_heads_beyond_32bit_offsets(nrc, oracle):
+    """A cache view whose heads lie more than 2 GiB apart from the first
+    (H = 8, one row per wave): the row form cannot address them from one
+    32-bit offset and takes the 64-bit address form. The device buffer spans
+    2.2 GB; the oracle writes a compact twin with the same block and page
+    strides, and each head's region plus a margin after it is compared."""
+    import torch
+    from norm_rope_cache_amd import synth
+
+    L, T, H, bs, nb = 1, 30, 8, 4, 9
+    bstr, pstr = bs * 136, 136
+    hs_big = 160_000_000                      # (H - 1) * hs_big * 2 bytes > 2^31
+    reg = (nb - 1) * bstr + (bs - 1) * pstr + 128 + 1024
+    hs_c = (reg + 7) // 8 * 8
+    rng = np.random.default_rng(77)
+    kv = synth.normal_bf16(7701, (L, T, 2 * H * 64), std=1.4)
+    pos = rng.integers(0, 64, T).astype(np.int64)
+    tab = synth.to_bf16_bits(rng.uniform(-1, 1, (64, 64)))
+    slots = [rng.permutation(nb * bs)[:T].astype(np.int64)]
+    compact = synth.random_bits_u16(7702, ((H - 1) * hs_c + reg,))
+    want = compact.copy()
+    oracle.context_kv_store_ex(kv, H, pos, slots, tab, [want], bs, nb, bstr, pstr, hs_c, 1e-6)
+    _say("store_ex heads 2.2 GB apart")
+    flat = torch.empty(((H - 1) * hs_big + reg,), dtype=torch.bfloat16, device="cuda")
+    for h in range(H):
+        flat[h * hs_big:h * hs_big + reg] = to_dev(compact[h * hs_c:h * hs_c + reg])
+    view = torch.as_strided(flat, (nb, H, bs, 128), (bstr, hs_big, pstr, 1))
+    nrc.context_kv_store_ex(to_dev(kv), to_dev(pos), [to_dev(s) for s in slots], to_dev(tab), [view], H, 1e-6)
+    torch.cuda.synchronize()
+    for h in range(H):
+        assert_bits_equal(to_host(flat[h * hs_big:h * hs_big + reg]), want[h * hs_c:h * hs_c + reg],
+                          f"store_ex far heads, head {h}")
+    del flat, view
+    torch.cuda.empty_cache()
+
 # --------------------------------------------------------------------- chain
 
 @pytest.mark.parametrize("fused", [False, True])
