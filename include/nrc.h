@@ -177,8 +177,8 @@ int32_t nrc_context_kv_project_ex(const uint16_t* normed, const uint16_t* w, int
  * nrc_context_kv_project_workspace_bytes - bytes of workspace the split form
  * of the projection needs for this shape on the current device, or 0 when
  * the shape is not split. Shapes whose output tiles are too few to occupy
- * the device's compute units split the D (summation) axis into 2, 4 or 8
- * slices (the projection is a stock bmm, whose summation order is free).
+ * the device's compute units split the D (summation) axis into 2 to 16
+ * slices, a power of two (the projection is a stock bmm, whose summation order is free).
  * Page "...runtime.draft", ContextKV._project. Returns a negative status
  * for shapes nrc_context_kv_project rejects.
  */

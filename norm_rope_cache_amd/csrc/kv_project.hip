@@ -563,27 +563,45 @@ int launch_tiles(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
 }
 
 // C = bf16(W[0] + W[1] + ... + W[S - 1]) element by element, the slices added
-// in order (deterministic); eight elements per thread, grid stride.
+// in order (deterministic); eight elements per thread, grid stride. S is a
+// template argument so that every slice's loads are issued before the first
+// add (one memory round trip per eight elements, not S).
+template <int S>
 __global__ __launch_bounds__(256) void kv_project_reduce_kernel(const float* __restrict__ W, uint16_t* __restrict__ C,
-                                                                int64_t count, int32_t S) {
+                                                                int64_t count) {
     for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < count; i += (int64_t)gridDim.x * 256 * 8) {
-        float acc[8];
-        {
-            const U32x4 a = load16(W + i), b = load16(W + i + 4);
-            const uint32_t p[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        U32x4 lo[S], hi[S];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = __uint_as_float(p[e]);
+        for (int k = 0; k < S; ++k) {
+            lo[k] = load16(W + (int64_t)k * count + i);
+            hi[k] = load16(W + (int64_t)k * count + i + 4);
         }
+        float acc[8] = {__uint_as_float(lo[0].x), __uint_as_float(lo[0].y), __uint_as_float(lo[0].z),
+                        __uint_as_float(lo[0].w), __uint_as_float(hi[0].x), __uint_as_float(hi[0].y),
+                        __uint_as_float(hi[0].z), __uint_as_float(hi[0].w)};
+#pragma unroll
         for (int k = 1; k < S; ++k) {
-            const float* w = W + (int64_t)k * count + i;
-            const U32x4 a = load16(w), b = load16(w + 4);
-            const uint32_t p[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            const uint32_t p[8] = {lo[k].x, lo[k].y, lo[k].z, lo[k].w, hi[k].x, hi[k].y, hi[k].z, hi[k].w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] = acc[e] + __uint_as_float(p[e]);
         }
         store16(C + i, U32x4{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]), pack_bf16(acc[4], acc[5]),
                              pack_bf16(acc[6], acc[7])});
     }
+}
+
+int launch_reduce(const ProjectArgs& a, int cus, hipStream_t stream) {
+    const int64_t count = (int64_t)a.L * a.M * a.N;
+    const int64_t blocks = (count / 8 + 255) / 256, cap = (int64_t)cus * 8;
+    const dim3 grid((unsigned)(blocks < cap ? blocks : cap));
+    switch (a.k_split) {
+        case 2: hipLaunchKernelGGL(kv_project_reduce_kernel<2>, grid, dim3(256), 0, stream, a.ws, a.C, count); break;
+        case 4: hipLaunchKernelGGL(kv_project_reduce_kernel<4>, grid, dim3(256), 0, stream, a.ws, a.C, count); break;
+        case 8: hipLaunchKernelGGL(kv_project_reduce_kernel<8>, grid, dim3(256), 0, stream, a.ws, a.C, count); break;
+        case 16: hipLaunchKernelGGL(kv_project_reduce_kernel<16>, grid, dim3(256), 0, stream, a.ws, a.C, count); break;
+        default: return -1;
+    }
+    return 0;
 }
 
 template <bool FUSED, bool PW, int CMODE, bool B_ND>
@@ -602,11 +620,7 @@ int launch_shape(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
                                ? launch_tiles<256, 256, 2, 4, false, false, 0, B_ND, true>(a, fa, stream)
                                : launch_tiles<128, 128, 2, 2, false, false, 0, B_ND, true>(a, fa, stream);
             if (rc) return rc;
-            const int64_t count = (int64_t)a.L * a.M * a.N;
-            const int64_t blocks = (count / 8 + 255) / 256, cap = (int64_t)cus * 8;
-            hipLaunchKernelGGL(kv_project_reduce_kernel, dim3((unsigned)(blocks < cap ? blocks : cap)), dim3(256), 0,
-                               stream, a.ws, a.C, count, a.k_split);
-            return 0;
+            return launch_reduce(a, cus, stream);
         }
     }
     return launch_tiles<128, 128, 2, 2, FUSED, PW, CMODE, B_ND, false>(a, fa, stream);
@@ -620,14 +634,18 @@ int32_t kv_project_k_split(int32_t L, int64_t M, int64_t K, int64_t N, int num_c
     if (N % 256 == 0 && big_tiles >= cus) return 1;
     // Slices of 256 x 256 tiles (N a multiple of 256, at least 256 rows) up
     // to one per CU, else of 128 x 128 tiles up to two per CU (their LDS ring
-    // lets two share a CU); at most 8 slices, each an even number (the loop
-    // takes two stages per trip) of at least 4 stages.
+    // lets two share a CU); each slice an even number (the loop takes two
+    // stages per trip) of at least 4 stages, at most 8 slices of 256 x 256
+    // tiles and 16 of 128 x 128 (measured: a 16-slice 256 x 256 split, whose
+    // partial sums double, ran 3% slower at 256 rows; the 128 x 128 splits
+    // gained 15-30% from 8 to 16 slices).
     const bool big = N % 256 == 0 && M >= 256;
     const int64_t tiles = big ? big_tiles : (int64_t)L * ((M + 127) / 128) * (N / 128);
     const int64_t target = big ? (int64_t)cus : 2 * (int64_t)cus;
     const int64_t nk = K / kBK;
     int32_t s = 1;
-    while (tiles * s < target && s < 8 && nk % (4 * s) == 0 && nk / (2 * s) >= 4) s *= 2;
+    const int32_t max_s = big ? 8 : 16;
+    while (tiles * s < target && s < max_s && nk % (4 * s) == 0 && nk / (2 * s) >= 4) s *= 2;
     return s;
 }
 

@@ -163,12 +163,18 @@ def test_project_split_workspace_and_argument_checks(lib):
     assert q(4, 16384, 8192, 1024) == 0
     # a 512-row prefill: 32 tiles of 256 x 256, eight slices
     assert q(4, 512, 8192, 1024) == 8 * 4 * 512 * 1024 * 4
+    # 256 rows: 16 tiles of 256 x 256, still eight slices (the cap for that tile)
+    assert q(4, 256, 8192, 1024) == 8 * 4 * 256 * 1024 * 4
     # 2000 rows: 128 tiles of 256 x 256, two slices
     assert q(4, 2000, 8192, 1024) == 2 * 4 * 2000 * 1024 * 4
-    # N = 384: 128 x 128 tiles (18 of them), eight slices
-    assert q(2, 300, 8192, 384) == 8 * 2 * 300 * 384 * 4
-    # 16 rows: eight slices at most
-    assert q(2, 16, 8192, 256) == 8 * 2 * 16 * 256 * 4
+    # N = 384: 128 x 128 tiles (18 of them), sixteen slices
+    assert q(2, 300, 8192, 384) == 16 * 2 * 300 * 384 * 4
+    # 16 rows: sixteen slices at most
+    assert q(2, 16, 8192, 256) == 16 * 2 * 16 * 256 * 4
+    # D = 1024 (32 stages): slices of at least 4 stages, an even number each
+    assert q(2, 16, 1024, 256) == 8 * 2 * 16 * 256 * 4
+    # D = 2048 (64 stages): sixteen slices of 4 stages
+    assert q(2, 16, 2048, 256) == 16 * 2 * 16 * 256 * 4
     assert q(4, 0, 8192, 1024) == 0
     assert q(0, 512, 8192, 1024) == EINVAL
     assert q(4, 512, 8100, 1024) == ENOTSUP

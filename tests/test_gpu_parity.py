@@ -514,9 +514,10 @@ def test_project_shapes(nrc, oracle, T, N, split):
 
 def _expected_k_split(L, T, N, cus=256, nk=256):
     """The split rule written out: none when 256 x 256 tiles fill the CUs;
-    else the smallest power of two (at most 8, each slice at least 4 stages
-    of 32) giving one 256 x 256 tile slice per CU (N a multiple of 256, at
-    least 256 rows) or two 128 x 128 tile slices per CU."""
+    else the smallest power of two (each slice an even number of at least 4
+    stages of 32) giving one 256 x 256 tile slice per CU (N a multiple of 256,
+    at least 256 rows; at most 8 slices) or two 128 x 128 tile slices per CU
+    (at most 16 slices)."""
     big_tiles = L * -(-T // 256) * (N // 256)
     if N % 256 == 0 and big_tiles >= cus:
         return 1
@@ -524,12 +525,12 @@ def _expected_k_split(L, T, N, cus=256, nk=256):
     tiles = big_tiles if big else L * -(-T // 128) * (N // 128)
     target = cus if big else 2 * cus
     s = 1
-    while tiles * s < target and s < 8 and nk % (2 * s) == 0 and nk // (2 * s) >= 4:
+    while tiles * s < target and s < (8 if big else 16) and nk % (4 * s) == 0 and nk // (2 * s) >= 4:
         s *= 2
     return s
 
 
-@pytest.mark.parametrize("L,T,N", [(4, 512, 1024), (1, 130, 128), (2, 300, 384), (2, 16, 256), (4, 2000, 1024),
+@pytest.mark.parametrize("L,T,N", [(4, 512, 1024), (4, 256, 1024), (1, 130, 128), (2, 300, 384), (2, 16, 256), (4, 2000, 1024),
                                    (1, 700, 512)])
 def test_project_split_summation(nrc, oracle, L, T, N):
     """Split summation: the workspace the library asks for follows the split
