@@ -257,7 +257,13 @@ __global__ __launch_bounds__(kBlockThreads) void context_norms_kernel(
             }
             continue;
         }
-        const bool fast_p = fast_h && finite(Sp) && finite(rp);
+        // The layer outputs take the paired conversion whenever Sp and rp are
+        // finite, however the hidden norm was rounded: a NaN or infinite h
+        // makes Sp NaN or infinite, so with a finite Sp every h is finite,
+        // |h rp| stays within about sqrt(8192), and with finite gains no
+        // product is NaN (a row whose hidden sum overflows has h = +-0 and
+        // still takes this path for all L outputs).
+        const bool fast_p = wfinite && finite(Sp) && finite(rp);
 #pragma unroll
         for (int k = 0; k < kFrags; ++k)
 #pragma unroll

@@ -360,7 +360,9 @@ __global__ __launch_bounds__(kBlockThreads) void norms_ex_lds_kernel(
             __syncthreads();
             const float Sp = combine(sums[slot][1]);
             const float rp = rsqrt_rn(__builtin_fmaf(Sp, 0x1p-13f, pre_eps));
-            const bool fast_p = fast_h && finite(Sp) && finite(rp);
+            // finite Sp: every h finite, whichever path rounded it (a NaN or
+            // infinite h makes the sum NaN or infinite), so no product is NaN
+            const bool fast_p = wfinite && finite(Sp) && finite(rp);
             auto layers_out = [&](auto fast) {
                 for (int l = 0; l < L; ++l)
 #pragma unroll
@@ -410,7 +412,10 @@ __global__ __launch_bounds__(kBlockThreads) void norms_ex_lds_kernel(
                             store_frag(l, k, y, fast);
                         }
                     };
-                    if (fast_h && finite(Sl) && finite(rl))
+                    // finite Sl: every g h finite (one NaN or infinite
+                    // product makes the sum NaN or infinite), whatever path
+                    // rounded h
+                    if (wfinite && finite(Sl) && finite(rl))
                         layer_out(std::true_type{});
                     else
                         layer_out(std::false_type{});
