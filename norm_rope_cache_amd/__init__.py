@@ -486,28 +486,63 @@ def context_kv_store(kv, positions, slots, cos_sin, caches, H, eps=1e-6, rows=No
 
     if k is None:
         _bf16(kv, "kv")
-        k, v = kv_views(kv, H)
-    for name, t in (("k", k), ("v", v)):
-        _bf16(t, name, contiguous=False)
-        if t.dim() != 4 or t.shape[2] != H or t.shape[3] != HEAD_DIM or t.stride(3) != 1 or t.stride(2) != HEAD_DIM:
-            raise ValueError(f"{name} must be an [L, T, H, 64] view with unit last stride and head stride 64")
-    L, T = k.shape[0], k.shape[1]
-    cache_list = list(caches) if not isinstance(caches, torch.Tensor) else [caches[i] for i in range(caches.shape[0])]
-    slot_list = list(slots) if not isinstance(slots, torch.Tensor) else [slots[i] for i in range(slots.shape[0])]
-    if len(cache_list) != L or len(slot_list) != L:
-        raise ValueError("one cache and one slot mapping per layer")
-    c0 = cache_list[0]
-    if c0.dim() != 4 or c0.shape[1] != H or c0.shape[3] != 2 * HEAD_DIM:
-        raise ValueError("caches must be [num_blocks, H, block_size, 128]")
-    nb, _, bs, _ = c0.shape
-    for c in cache_list:
-        _bf16(c, "cache")
-        if c.shape != c0.shape:
-            raise ValueError("all caches must have one shape")
-    n_rows = slot_list[0].shape[0] if rows is None else rows
-    for s in slot_list:
-        if s.dtype != torch.int64 or s.dim() != 1 or not s.is_contiguous() or s.shape[0] != slot_list[0].shape[0]:
+        if kv.dim() != 3 or kv.shape[2] != 2 * H * HEAD_DIM:
+            raise ValueError("kv must be [L, T, 2 H 64]")
+        # K and V are the two halves of each contiguous kv row
+        L, T = kv.shape[0], kv.shape[1]
+        k_ptr = kv.data_ptr()
+        v_ptr = k_ptr + H * HEAD_DIM * 2
+        k_ls = v_ls = kv.stride(0)
+        k_rs = v_rs = kv.stride(1)
+    else:
+        for name, t in (("k", k), ("v", v)):
+            _bf16(t, name, contiguous=False)
+            if t.dim() != 4 or t.shape[2] != H or t.shape[3] != HEAD_DIM or t.stride(3) != 1 or t.stride(2) != HEAD_DIM:
+                raise ValueError(f"{name} must be an [L, T, H, 64] view with unit last stride and head stride 64")
+        L, T = k.shape[0], k.shape[1]
+        k_ptr, v_ptr = k.data_ptr(), v.data_ptr()
+        k_ls, k_rs, v_ls, v_rs = k.stride(0), k.stride(1), v.stride(0), v.stride(1)
+    # Per-layer pointers: a contiguous stacked tensor is addressed by its
+    # layer stride (no per-layer views); lists and other tensors layer by layer.
+    if isinstance(caches, torch.Tensor) and caches.dim() == 5 and caches.is_contiguous():
+        _bf16(caches, "cache")
+        if caches.shape[0] != L:
+            raise ValueError("one cache and one slot mapping per layer")
+        if caches.shape[2] != H or caches.shape[4] != 2 * HEAD_DIM:
+            raise ValueError("caches must be [num_blocks, H, block_size, 128]")
+        nb, bs = caches.shape[1], caches.shape[3]
+        c_base, c_step = caches.data_ptr(), caches.stride(0) * 2
+        cache_ptrs = [c_base + i * c_step for i in range(L)]
+    else:
+        cache_list = list(caches) if not isinstance(caches, torch.Tensor) else [caches[i] for i in range(caches.shape[0])]
+        if len(cache_list) != L:
+            raise ValueError("one cache and one slot mapping per layer")
+        c0 = cache_list[0]
+        if c0.dim() != 4 or c0.shape[1] != H or c0.shape[3] != 2 * HEAD_DIM:
+            raise ValueError("caches must be [num_blocks, H, block_size, 128]")
+        nb, _, bs, _ = c0.shape
+        for c in cache_list:
+            _bf16(c, "cache")
+            if c.shape != c0.shape:
+                raise ValueError("all caches must have one shape")
+        cache_ptrs = [c.data_ptr() for c in cache_list]
+    if isinstance(slots, torch.Tensor) and slots.dim() == 2 and slots.is_contiguous():
+        if slots.dtype != torch.int64:
             raise ValueError("slots must be contiguous int64 [rows] tensors of one length")
+        if slots.shape[0] != L:
+            raise ValueError("one cache and one slot mapping per layer")
+        n_rows = slots.shape[1] if rows is None else rows
+        s_base, s_step = slots.data_ptr(), slots.stride(0) * 8
+        slot_ptrs = [s_base + i * s_step for i in range(L)]
+    else:
+        slot_list = list(slots) if not isinstance(slots, torch.Tensor) else [slots[i] for i in range(slots.shape[0])]
+        if len(slot_list) != L:
+            raise ValueError("one cache and one slot mapping per layer")
+        n_rows = slot_list[0].shape[0] if rows is None else rows
+        for s in slot_list:
+            if s.dtype != torch.int64 or s.dim() != 1 or not s.is_contiguous() or s.shape[0] != slot_list[0].shape[0]:
+                raise ValueError("slots must be contiguous int64 [rows] tensors of one length")
+        slot_ptrs = [s.data_ptr() for s in slot_list]
     if cos_sin is not None:
         _bf16(cos_sin, "cos_sin")
         if cos_sin.dim() != 2 or cos_sin.shape[1] != HEAD_DIM:
@@ -516,11 +551,11 @@ def context_kv_store(kv, positions, slots, cos_sin, caches, H, eps=1e-6, rows=No
             raise ValueError("positions must be a contiguous int64 tensor")
         if positions.shape[0] < n_rows:
             raise ValueError("positions shorter than the inserted rows")
-    slot_arr = (_vp * L)(*[s.data_ptr() for s in slot_list])
-    cache_arr = (_vp * L)(*[c.data_ptr() for c in cache_list])
+    slot_arr = (_vp * L)(*slot_ptrs)
+    cache_arr = (_vp * L)(*cache_ptrs)
     max_pos = 0 if cos_sin is None else cos_sin.shape[0]
     _check(_load().nrc_context_kv_store(
-        _ptr(k), _ptr(v), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
+        ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), k_ls, k_rs, v_ls, v_rs,
         _ptr(positions) if cos_sin is not None else None, slot_arr, n_rows, T, _ptr(cos_sin), max_pos, cache_arr,
         nb, bs, H, L, eps, _stream(stream)))
 
