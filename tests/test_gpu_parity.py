@@ -827,6 +827,42 @@ def test_store_shapes(nrc, oracle, L, H, bs, nb):
         assert_bits_equal(to_host(cd), want, f"store L={L} H={H} bs={bs} eps={eps}")
 
 
+def test_store_operand_forms(nrc, oracle):
+    """The store call's operand forms give the same cache: stacked caches and
+    slot rows (addressed by their layer stride), lists of per-layer tensors,
+    and stacked tensors with padded layer strides (taken layer by layer)."""
+    import torch
+    from norm_rope_cache_amd import synth
+
+    L, T, H, bs, nb = 3, 40, 8, 16, 8
+    kv = synth.normal_bf16(7101, (L, T, 2 * H * 64), std=1.3)
+    rng = np.random.default_rng(71)
+    slots = np.stack([rng.permutation(nb * bs)[:T] for _ in range(L)]).astype(np.int64)
+    slots[1, 5] = -1
+    positions = rng.integers(0, 64, T).astype(np.int64)
+    tab = synth.rope_table(64)
+    caches = synth.random_bits_u16(7102, (L, nb, H, bs, 128))
+    want = caches.copy()
+    oracle.context_kv_store(kv, H, positions, slots, tab, want, bs, 1e-6)
+    kv_d, pos_d, tab_d = to_dev(kv), to_dev(positions), to_dev(tab)
+    _say("store operand forms")
+    stacked, slots_d = to_dev(caches), to_dev(slots)
+    nrc.context_kv_store(kv_d, pos_d, slots_d, tab_d, stacked, H, 1e-6)
+    assert_bits_equal(to_host(stacked), want, "store, stacked caches and slots")
+    listed = [to_dev(caches[l]) for l in range(L)]
+    nrc.context_kv_store(kv_d, pos_d, [to_dev(slots[l]) for l in range(L)], tab_d, listed, H, 1e-6)
+    for l in range(L):
+        assert_bits_equal(to_host(listed[l]), want[l], f"store, listed caches, layer {l}")
+    padded_c = torch.zeros((L, nb + 1, H, bs, 128), dtype=torch.bfloat16, device="cuda")
+    padded_c[:, :nb] = to_dev(caches)
+    padded_s = torch.full((L, T + 3), -1, dtype=torch.int64, device="cuda")
+    padded_s[:, :T] = slots_d
+    nrc.context_kv_store(kv_d, pos_d, padded_s[:, :T], tab_d, padded_c[:, :nb], H, 1e-6)
+    got = to_host(padded_c)
+    assert_bits_equal(got[:, :nb], want, "store, padded layer strides")
+    assert np.all(got[:, nb:] == 0), "store wrote past a layer's cache"
+
+
 def test_store_strided_views(nrc, oracle):
     """k and v as views with padded row and layer strides."""
     from norm_rope_cache_amd import synth
