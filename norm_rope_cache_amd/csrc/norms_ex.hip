@@ -176,9 +176,6 @@ constexpr int kLayerLds = 128 * 1024;  // layer weights staged in LDS up to this
 constexpr int kMaxLdsLayers = kLayerLds / (kHidden * 2);
 
 __device__ __forceinline__ bool finite(float v) { return __builtin_fabsf(v) < __builtin_huge_valf(); }
-__device__ __forceinline__ bool finite_bf16_pair(uint32_t w) {
-    return (w & 0x7F80u) != 0x7F80u && (w & 0x7F800000u) != 0x7F800000u;
-}
 
 // HK: hidden weight kind (0 none, 1 bf16, 2 FP32). LF: layer weights in
 // LDS as 0 - none; 1 - the stored bf16 (center added at use); 2 - FP32 gains
