@@ -146,6 +146,17 @@ def _bf16(t, name, contiguous=True):
     return t
 
 
+def _same_device(t, ref, name):
+    """Raise unless t is a tensor on ref's GPU: a host pointer handed to a
+    kernel would fault the device instead of failing."""
+    import torch
+
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != ref.device:
+        where = "not a tensor" if not isinstance(t, torch.Tensor) else str(t.device)
+        raise ValueError(f"{name} must be a tensor on {ref.device} ({where})")
+    return t
+
+
 def context_norms(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hidden_center=0.0, pre_center=0.0,
                   out=None, stream=None):
     """stack([pre_norm_l(hidden_norm(x)) for l]): x [T, 8192] bf16 ->
@@ -292,6 +303,8 @@ def context_hidden_norm(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hi
     _bf16(h, "h")
     if tuple(h.shape) != (T, D) or r.dtype != torch.float32 or tuple(r.shape) != (T,) or not r.is_contiguous():
         raise ValueError("h must be [T, D] bf16 and r [T] float32")
+    _same_device(h, x, "h")
+    _same_device(r, x, "r")
     _check(_load().nrc_context_hidden_norm(_ptr(x), T, D, _ptr(hidden_w), _ptr(pre_w), L, hidden_eps, pre_eps,
                                            hidden_center, pre_center, _ptr(h), _ptr(r), _stream(stream)))
     return h, r
@@ -314,10 +327,15 @@ def context_kv_project_fused(h, r, pre_w, w_kv, pre_center=0.0, out=None, stream
             raise ValueError("pre_w must be [L, D]")
     if r.dtype != torch.float32 or tuple(r.shape) != (T,) or not r.is_contiguous():
         raise ValueError("r must be a contiguous float32 [T]")
+    _same_device(r, h, "r")
+    _same_device(w_kv, h, "w_kv")
+    if pre_w is not None:
+        _same_device(pre_w, h, "pre_w")
     if out is None:
         out = torch.empty((L, T, N), dtype=torch.bfloat16, device=h.device)
     else:
         _bf16(out, "out")
+        _same_device(out, h, "out")
         if tuple(out.shape) != (L, T, N):
             raise ValueError("out must be [L, T, N]")
     _check(_load().nrc_context_kv_project_fused(_ptr(h), _ptr(r), _ptr(pre_w), pre_center, _ptr(w_kv), _ptr(out), L,
@@ -331,6 +349,7 @@ def _project_operands(normed, w_kv, out, w_layout):
 
     _bf16(normed, "normed")
     _bf16(w_kv, "w_kv")
+    _same_device(w_kv, normed, "w_kv")
     L, T, D = normed.shape
     if w_layout == "dn":
         if w_kv.dim() != 3 or w_kv.shape[0] != L or w_kv.shape[1] != D:
@@ -346,6 +365,7 @@ def _project_operands(normed, w_kv, out, w_layout):
         out = torch.empty((L, T, N), dtype=torch.bfloat16, device=normed.device)
     else:
         _bf16(out, "out")
+        _same_device(out, normed, "out")
         if tuple(out.shape) != (L, T, N):
             raise ValueError("out must be [L, T, N]")
     return L, T, D, N, (0 if w_layout == "dn" else 1), out
@@ -428,6 +448,7 @@ def context_kv_store_ex(kv, positions, slots, cos_sin, caches, H, eps=1e-6, k=No
         if t.dim() != 4 or t.shape[2] != H or t.shape[3] != HEAD_DIM or t.stride(3) != 1 or t.stride(2) != HEAD_DIM:
             raise ValueError(f"{name} must be an [L, T, H, 64] view with unit last stride and head stride 64")
     L, T = k.shape[0], k.shape[1]
+    _same_device(v, k, "v")
     slot_list, cache_list = list(slots), list(caches)
     if len(slot_list) != L or len(cache_list) != L:
         raise ValueError("one cache and one slot list (or None) per layer")
@@ -440,6 +461,7 @@ def context_kv_store_ex(kv, positions, slots, cos_sin, caches, H, eps=1e-6, k=No
     for c in live:
         if c is None or c.dtype != torch.bfloat16 or not c.is_cuda:
             raise ValueError("every layer with slots needs a bf16 device cache")
+        _same_device(c, k, "caches")
         if c.shape != c0.shape or c.stride() != c0.stride():
             raise ValueError("all caches must have one shape and one stride")
     nb, _, bs, _ = c0.shape
@@ -448,15 +470,18 @@ def context_kv_store_ex(kv, positions, slots, cos_sin, caches, H, eps=1e-6, k=No
         if s is None:
             rows.append(0)
             continue
-        if s.dtype != torch.int64 or s.dim() != 1 or not s.is_contiguous():
+        if not isinstance(s, torch.Tensor) or s.dtype != torch.int64 or s.dim() != 1 or not s.is_contiguous():
             raise ValueError("slots must be contiguous int64 [rows] tensors")
+        _same_device(s, k, "slots")
         rows.append(s.shape[0])
     if cos_sin is not None:
         _bf16(cos_sin, "cos_sin")
+        _same_device(cos_sin, k, "cos_sin")
         if cos_sin.dim() != 2 or cos_sin.shape[1] != HEAD_DIM:
             raise ValueError("cos_sin must be [max_position, 64]")
         if positions is None or positions.dtype != torch.int64 or not positions.is_contiguous():
             raise ValueError("positions must be a contiguous int64 tensor")
+        _same_device(positions, k, "positions")
         if positions.shape[0] < max(rows):
             raise ValueError("positions shorter than the inserted rows")
     slot_arr = (_vp * L)(*[None if s is None else s.data_ptr() for s in slot_list])
@@ -477,7 +502,10 @@ def context_kv_store(kv, positions, slots, cos_sin, caches, H, eps=1e-6, rows=No
     kv       [L, T, 2 H 64] bf16 projection output (or pass k, v views
              [L, T, H, 64] with unit last stride and head stride 64)
     positions [T] int64 (unused without cos_sin)
-    slots    [L, rows] int64 tensor or a list of L [rows] int64 tensors
+    slots    [rows] int64 tensor (one mapping shared by every layer), an
+             [L, rows] int64 tensor or a list of L [rows] int64 tensors
+    rows     the first `rows` rows are inserted (default: the mapping's
+             length; at most that length and T)
     cos_sin  [max_position, 64] bf16 or None (RoPE off)
     caches   [L, num_blocks, H, block_size, 128] bf16 tensor or a list of L
              [num_blocks, H, block_size, 128] tensors
@@ -500,12 +528,15 @@ def context_kv_store(kv, positions, slots, cos_sin, caches, H, eps=1e-6, rows=No
             if t.dim() != 4 or t.shape[2] != H or t.shape[3] != HEAD_DIM or t.stride(3) != 1 or t.stride(2) != HEAD_DIM:
                 raise ValueError(f"{name} must be an [L, T, H, 64] view with unit last stride and head stride 64")
         L, T = k.shape[0], k.shape[1]
+        _same_device(v, k, "v")
         k_ptr, v_ptr = k.data_ptr(), v.data_ptr()
         k_ls, k_rs, v_ls, v_rs = k.stride(0), k.stride(1), v.stride(0), v.stride(1)
+    kv_ref = kv if k is None else k
     # Per-layer pointers: a contiguous stacked tensor is addressed by its
     # layer stride (no per-layer views); lists and other tensors layer by layer.
     if isinstance(caches, torch.Tensor) and caches.dim() == 5 and caches.is_contiguous():
         _bf16(caches, "cache")
+        _same_device(caches, kv_ref, "caches")
         if caches.shape[0] != L:
             raise ValueError("one cache and one slot mapping per layer")
         if caches.shape[2] != H or caches.shape[4] != 2 * HEAD_DIM:
@@ -523,32 +554,48 @@ def context_kv_store(kv, positions, slots, cos_sin, caches, H, eps=1e-6, rows=No
         nb, _, bs, _ = c0.shape
         for c in cache_list:
             _bf16(c, "cache")
+            _same_device(c, kv_ref, "caches")
             if c.shape != c0.shape:
                 raise ValueError("all caches must have one shape")
         cache_ptrs = [c.data_ptr() for c in cache_list]
-    if isinstance(slots, torch.Tensor) and slots.dim() == 2 and slots.is_contiguous():
+    if isinstance(slots, torch.Tensor) and slots.dim() == 1:
+        # one mapping shared by every layer: each layer's pointer is the same array
+        if slots.dtype != torch.int64 or not slots.is_contiguous():
+            raise ValueError("slots must be contiguous int64 [rows] tensors of one length")
+        _same_device(slots, kv_ref, "slots")
+        slot_len = slots.shape[0]
+        slot_ptrs = [slots.data_ptr()] * L
+    elif isinstance(slots, torch.Tensor) and slots.dim() == 2 and slots.is_contiguous():
         if slots.dtype != torch.int64:
             raise ValueError("slots must be contiguous int64 [rows] tensors of one length")
         if slots.shape[0] != L:
             raise ValueError("one cache and one slot mapping per layer")
-        n_rows = slots.shape[1] if rows is None else rows
+        _same_device(slots, kv_ref, "slots")
+        slot_len = slots.shape[1]
         s_base, s_step = slots.data_ptr(), slots.stride(0) * 8
         slot_ptrs = [s_base + i * s_step for i in range(L)]
     else:
         slot_list = list(slots) if not isinstance(slots, torch.Tensor) else [slots[i] for i in range(slots.shape[0])]
         if len(slot_list) != L:
             raise ValueError("one cache and one slot mapping per layer")
-        n_rows = slot_list[0].shape[0] if rows is None else rows
         for s in slot_list:
-            if s.dtype != torch.int64 or s.dim() != 1 or not s.is_contiguous() or s.shape[0] != slot_list[0].shape[0]:
+            if (not isinstance(s, torch.Tensor) or s.dtype != torch.int64 or s.dim() != 1 or not s.is_contiguous()
+                    or s.shape[0] != slot_list[0].shape[0]):
                 raise ValueError("slots must be contiguous int64 [rows] tensors of one length")
+            _same_device(s, kv_ref, "slots")
+        slot_len = slot_list[0].shape[0]
         slot_ptrs = [s.data_ptr() for s in slot_list]
+    n_rows = slot_len if rows is None else int(rows)
+    if n_rows < 0 or n_rows > slot_len:
+        raise ValueError(f"rows = {n_rows} must lie in [0, {slot_len}] (the slot mapping's length)")
     if cos_sin is not None:
         _bf16(cos_sin, "cos_sin")
+        _same_device(cos_sin, kv_ref, "cos_sin")
         if cos_sin.dim() != 2 or cos_sin.shape[1] != HEAD_DIM:
             raise ValueError("cos_sin must be [max_position, 64]")
         if positions is None or positions.dtype != torch.int64 or not positions.is_contiguous():
             raise ValueError("positions must be a contiguous int64 tensor")
+        _same_device(positions, kv_ref, "positions")
         if positions.shape[0] < n_rows:
             raise ValueError("positions shorter than the inserted rows")
     slot_arr = (_vp * L)(*slot_ptrs)

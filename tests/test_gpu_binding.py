@@ -1,0 +1,96 @@
+"""The Python binding refuses operands that would hand a kernel a host
+pointer or an out-of-range row count, before anything is launched."""
+
+import numpy as np
+import pytest
+
+from helpers import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def nrc():
+    import norm_rope_cache_amd as m
+
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    m._load()
+    return m
+
+
+def _store_operands(L=2, T=8, H=8, nb=4, bs=16):
+    from norm_rope_cache_amd import synth
+
+    kv = to_dev(synth.normal_bf16(51, (L, T, 2 * H * 64)))
+    pos = torch.arange(T, dtype=torch.int64)
+    slots = torch.arange(T, dtype=torch.int64)
+    cs = to_dev(synth.rope_table(64))
+    caches = to_dev(synth.random_bits_u16(52, (L, nb, H, bs, 128)))
+    return kv, pos, slots, cs, caches, H
+
+
+def test_store_refuses_host_slots_positions_and_long_rows(nrc):
+    kv, pos, slots, cs, caches, H = _store_operands()
+    before = to_host(caches)
+    L = kv.shape[0]
+    cases = {
+        "host slots (shared)": dict(positions=pos.cuda(), slots=slots),
+        "host slots (stacked)": dict(positions=pos.cuda(), slots=slots.expand(L, -1).contiguous()),
+        "host slots (list)": dict(positions=pos.cuda(), slots=[slots, slots]),
+        "host positions": dict(positions=pos, slots=slots.cuda()),
+        "rows beyond the mapping": dict(positions=pos.cuda(), slots=slots[:5].cuda(), rows=6),
+        "negative rows": dict(positions=pos.cuda(), slots=slots.cuda(), rows=-1),
+    }
+    for what, kw in cases.items():
+        with pytest.raises(ValueError):
+            nrc.context_kv_store(kv, kw["positions"], kw["slots"], cs, caches, H, rows=kw.get("rows"))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(caches), before), "a refused call wrote the cache"
+
+
+def test_store_ex_refuses_host_slots_and_positions(nrc):
+    kv, pos, slots, cs, caches, H = _store_operands()
+    before = to_host(caches)
+    views = [caches[0], caches[1]]
+    with pytest.raises(ValueError):
+        nrc.context_kv_store_ex(kv, pos.cuda(), [slots, slots.cuda()], cs, views, H)
+    with pytest.raises(ValueError):
+        nrc.context_kv_store_ex(kv, pos, [slots.cuda(), slots.cuda()], cs, views, H)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(caches), before), "a refused call wrote the cache"
+
+
+def test_fused_projection_refuses_a_host_scale(nrc):
+    from norm_rope_cache_amd import synth
+
+    T, L, N = 4, 1, 128
+    h = to_dev(synth.normal_bf16(61, (T, 8192)))
+    w = to_dev(synth.normal_bf16(62, (L, 8192, N), std=0.02))
+    out = torch.zeros((L, T, N), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        nrc.context_kv_project_fused(h, torch.ones(T, dtype=torch.float32), None, w, out=out)
+    with pytest.raises(ValueError):
+        nrc.context_hidden_norm(h, None, None, L, r=torch.empty(T, dtype=torch.float32))
+    torch.cuda.synchronize()
+    assert not bool(out.view(torch.int16).any()), "a refused call wrote the output"
+
+
+def test_shared_slot_mapping_equals_stacked_copies(nrc):
+    """One [rows] mapping handed to every layer writes what L identical
+    copies write."""
+    from norm_rope_cache_amd import synth
+
+    kv, pos, _, cs, caches, H = _store_operands(L=3, T=40, nb=8)
+    slots = torch.from_numpy(synth.permutation(7, 8 * 16)[:40].copy()).cuda()
+    slots[5] = -1
+    a, b = caches.clone(), caches.clone()
+    nrc.context_kv_store(kv, torch.arange(40, dtype=torch.int64, device="cuda"), slots, to_dev(synth.rope_table(64)),
+                         a, H)
+    nrc.context_kv_store(kv, torch.arange(40, dtype=torch.int64, device="cuda"), slots.expand(3, -1).contiguous(),
+                         to_dev(synth.rope_table(64)), b, H)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(a), to_host(b))
+    assert not np.array_equal(to_host(a), to_host(caches))
