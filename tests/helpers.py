@@ -63,3 +63,29 @@ def projection_tolerance_ok(C, Cstar, rel=1e-2):
         i = tuple(int(v) for v in np.argwhere(err > lim)[0])
         return False, f"element {i}: |{Cd[i]} - {Cs[i]}| > {lim[i]}"
     return True, ""
+
+
+def oracle_norms_chunked(oracle, x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, chunk=1024, each=None):
+    """The oracle's norms over row chunks on a thread pool (the oracle's C
+    routine releases the GIL; each row is normalised on its own, so chunking
+    changes nothing). Returns [L, T, 8192] bf16 bits, or, with `each`, calls
+    each(r0, r1, out_chunk) per chunk instead of assembling the whole output."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    T = x.shape[0]
+    starts = list(range(0, T, chunk))
+    out = None if each is not None else np.empty((L, T, x.shape[1]), dtype=np.uint16)
+
+    def one(r0):
+        r1 = min(T, r0 + chunk)
+        o = oracle.context_norms(np.ascontiguousarray(x[r0:r1]), hidden_w, pre_w, L, hidden_eps, pre_eps)
+        if each is not None:
+            each(r0, r1, o)
+        else:
+            out[:, r0:r1] = o
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(one, starts))
+    return out
