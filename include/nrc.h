@@ -204,6 +204,31 @@ int32_t nrc_context_kv_project_split(const uint16_t* normed, const uint16_t* w, 
                                      int32_t L, int64_t T, int64_t D, int64_t N, void* workspace,
                                      int64_t workspace_bytes, void* stream);
 
+/* Bytes of device scratch behind nrc_context_kv_project_noalloc (one copy per GPU). */
+#define NRC_PROJECT_SCRATCH_BYTES (64LL << 20)
+
+/*
+ * nrc_context_kv_project_noalloc - nrc_context_kv_project_split for callers
+ * that cannot allocate device memory (code under graph capture, serving loops
+ * and harnesses that forbid allocation): the split form's FP32 partial sums
+ * go to a scratch array the library holds on each GPU (NRC_PROJECT_SCRATCH_BYTES,
+ * taken when the library is first used on that GPU and held until the
+ * process ends) instead of a caller workspace. Same kernels, split rule and
+ * bits as nrc_context_kv_project_split; shapes that do not split run the
+ * one-pass kernel and touch no scratch. The call allocates nothing.
+ *
+ *   Arguments as nrc_context_kv_project_ex; the caller owns every operand.
+ *   Errors as nrc_context_kv_project_ex, plus NRC_EINVAL when the shape's
+ *   split needs more than NRC_PROJECT_SCRATCH_BYTES (nothing is launched)
+ *   and NRC_EIO when the scratch has no address on the current device.
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *   time on one GPU (other streams, other threads) race and must be ordered
+ *   by the caller. Each call writes every scratch element it reads, so no
+ *   state carries over between calls.
+ */
+int32_t nrc_context_kv_project_noalloc(const uint16_t* normed, const uint16_t* w, int32_t w_layout, uint16_t* kv,
+                                       int32_t L, int64_t T, int64_t D, int64_t N, void* stream);
+
 /*
  * nrc_context_kv_project_timed - nrc_context_kv_project_ex (one pass, never
  * split) that also records, per workgroup, the shader clock counter

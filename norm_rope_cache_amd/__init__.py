@@ -31,6 +31,7 @@ __all__ = [
     "context_kv_chain",
     "context_hidden_norm",
     "context_kv_project_fused",
+    "context_kv_project_noalloc",
     "kv_views",
     "check_scalars",
     "check_bf16_pair",
@@ -93,6 +94,8 @@ def _load():
     L.nrc_context_kv_project_workspace_bytes.argtypes = [_i32, _i64, _i64, _i64]
     L.nrc_context_kv_project_split.restype = _i32
     L.nrc_context_kv_project_split.argtypes = [_vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp]
+    L.nrc_context_kv_project_noalloc.restype = _i32
+    L.nrc_context_kv_project_noalloc.argtypes = [_vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp]
     L.nrc_context_kv_project_timed.restype = _i32
     L.nrc_context_kv_project_timed.argtypes = [_vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _vp,
                                                _vp]
@@ -394,6 +397,20 @@ def context_kv_project(normed, w_kv, out=None, stream=None, w_layout="dn", split
         _check(lib.nrc_context_kv_project(_ptr(normed), _ptr(w_kv), _ptr(out), L, T, D, N, _stream(stream)))
     else:
         _check(lib.nrc_context_kv_project_ex(_ptr(normed), _ptr(w_kv), 1, _ptr(out), L, T, D, N, _stream(stream)))
+    return out
+
+
+def context_kv_project_noalloc(normed, w_kv, out, stream=None, w_layout="dn"):
+    """context_kv_project for callers that cannot allocate: the split form's
+    partial sums go to the library's per-GPU scratch (no workspace, no
+    allocation by the library or here; `out` is required). Same bits as
+    context_kv_project; raises NrcError for a split needing more scratch
+    than the library holds. Calls that overlap on one GPU race."""
+    if out is None:
+        raise ValueError("context_kv_project_noalloc writes into a caller-owned out")
+    L, T, D, N, layout, out = _project_operands(normed, w_kv, out, w_layout)
+    _check(_load().nrc_context_kv_project_noalloc(_ptr(normed), _ptr(w_kv), layout, _ptr(out), L, T, D, N,
+                                                  _stream(stream)))
     return out
 
 

@@ -251,6 +251,23 @@ int32_t nrc_context_kv_project_split(const uint16_t* normed, const uint16_t* w, 
     return project_impl(normed, w, w_layout, kv, L, T, D, N, workspace, workspace_bytes, true, stream);
 }
 
+static_assert(NRC_PROJECT_SCRATCH_BYTES == nrc::kProjectScratchBytes, "header and library scratch sizes differ");
+
+int32_t nrc_context_kv_project_noalloc(const uint16_t* normed, const uint16_t* w, int32_t w_layout, uint16_t* kv,
+                                       int32_t L, int64_t T, int64_t D, int64_t N, void* stream) {
+    if (int32_t rc = project_shape_ok(L, T, D, N)) return rc;
+    const int64_t need = T == 0 ? 0 : project_workspace_bytes(L, T, D, N);
+    if (need > nrc::kProjectScratchBytes)
+        return fail(NRC_EINVAL,
+                    "context_kv_project_noalloc: this shape's split needs %lld bytes of scratch, more than the %lld "
+                    "the library holds (use nrc_context_kv_project_split with a workspace)",
+                    (long long)need, (long long)nrc::kProjectScratchBytes);
+    void* ws = nullptr;
+    if (need > 0 && nrc::project_scratch(&ws) != 0)
+        return fail(NRC_EIO, "context_kv_project_noalloc: no address for the device scratch on the current device");
+    return project_impl(normed, w, w_layout, kv, L, T, D, N, ws, need, true, stream);
+}
+
 int32_t nrc_context_kv_project_timed(const uint16_t* normed, const uint16_t* w, int32_t w_layout, uint16_t* kv,
                                      int32_t L, int64_t T, int64_t D, int64_t N, uint64_t* stamps,
                                      int64_t stamps_len, int32_t* workgroups, int32_t* wall_khz, void* stream) {

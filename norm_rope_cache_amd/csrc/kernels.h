@@ -124,6 +124,11 @@ struct ProjectArgs {
 };
 
 int launch_kv_project(const ProjectArgs& a, hipStream_t stream);
+// Bytes of the device-resident scratch behind the no-allocation projection.
+constexpr int64_t kProjectScratchBytes = (int64_t)64 << 20;
+// This GPU's (the current device's) address of that scratch; looked up once
+// per device. 0 on success.
+int project_scratch(void** ptr);
 // Number of K slices the projection of this shape is split into (1: none):
 // only shapes with too few output tiles to fill the CUs are split.
 int32_t kv_project_k_split(int32_t L, int64_t M, int64_t K, int64_t N, int num_cus);

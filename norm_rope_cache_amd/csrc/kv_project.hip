@@ -27,12 +27,20 @@
 //   - consecutive tile ids go to one XCD (workgroup ids are dealt
 //     round-robin over the 8 XCDs), so tiles sharing an A panel or a B panel
 //     meet in one L2.
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
 
 namespace nrc {
+
+// Scratch of the no-allocation projection: the split form's FP32 partial
+// sums for callers that cannot allocate device memory. One copy per GPU,
+// held from the library's first use on that GPU until the process ends; host
+// code reaches it only through the address hipGetSymbolAddress returns for
+// the current device (project_scratch), never through this name.
+static __device__ __align__(256) float scratch[kProjectScratchBytes / sizeof(float)];
 
 namespace {
 
@@ -647,6 +655,22 @@ int32_t kv_project_k_split(int32_t L, int64_t M, int64_t K, int64_t N, int num_c
     const int32_t max_s = big ? 8 : 16;
     while (tiles * s < target && s < max_s && nk % (4 * s) == 0 && nk / (2 * s) >= 4) s *= 2;
     return s;
+}
+
+int project_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return -1;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return 0;
 }
 
 int launch_kv_project(const ProjectArgs& a, hipStream_t stream) {
