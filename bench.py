@@ -39,16 +39,16 @@ def algorithmic_bytes(cfg, slots_np):
 
     norms: read x once (2 D per row), write L rows (2 L D per row), plus the
            weights once ((1 + L) 2 D, or none when weightless).
-    store: 8 B of slot per (layer, row); per inserted (layer, row): 8 B of
-           position + 128 B of cos/sin with RoPE, K and V read (2 N) and
-           written (2 N). Rows with a negative slot read nothing else."""
-    import numpy as np
-
+    store: the one slot mapping every layer shares, 8 B per row, and with
+           RoPE each row's position (8 B, loaded with the slot); per row with
+           a slot: its cos/sin row (128 B) once, and per layer K and V read
+           (2 N) and written (2 N). Rows with a negative slot read nothing
+           else."""
     D, L, T, N = 8192, cfg.L, cfg.T, cfg.N
     w = (1 if cfg.hidden_weighted else 0) * 2 * D + (L if cfg.pre_weighted else 0) * 2 * D
     norms = T * (2 * D + 2 * L * D) + w
-    valid = int((slots_np >= 0).sum())  # over all layers
-    store = 8 * L * T + valid * (2 * N + 2 * N + ((8 + 128) if cfg.rope else 0))
+    valid = int((slots_np >= 0).sum())  # rows of the shared mapping with a slot
+    store = T * (8 + (8 if cfg.rope else 0)) + valid * (128 if cfg.rope else 0) + valid * L * (2 * N + 2 * N)
     flops = 2 * L * T * D * N
     return norms, store, flops
 
@@ -73,22 +73,74 @@ def traffic_from_profiles(kernel_tag):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(d, cfg, rows):
-    """The CPU oracle as it stands (single thread), on the first `rows` rows
-    of the workload: norms, projection, store. Returns rows/s."""
+def host_cpu():
+    """(threads available to this process, CPU model name)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    # the box's CPU share for one GPU is what OMP_NUM_THREADS says, if set
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
+def cpu_baseline(d, cfg, rows, threads):
+    """The CPU oracle as it stands, on the first `rows` rows of the workload,
+    stage by stage, each stage's work spread over `threads` host threads
+    (the oracle's C routines release the GIL): norms by row blocks, the FP32
+    projection by (layer, row block), the store by (layer, row block) into
+    that layer's cache (distinct slots: no two tasks write one cell).
+    Returns per-stage seconds."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import oracle
 
-    x = np.ascontiguousarray(d["x"][:rows])
-    pos = d["positions"][:rows]
+    L, N, H = cfg.L, cfg.N, cfg.H
+    x = d["x"][:rows]
+    pos = np.ascontiguousarray(d["positions"][:rows])
     slots = np.ascontiguousarray(d["slots"][:, :rows])
     caches = d["caches_host_sample"]
-    t0 = time.perf_counter()
-    oracle.chain(x, d["hidden_w"], d["pre_w"], cfg.L, d["w_kv"], cfg.H, pos, slots, d["cos_sin"], caches,
-                 cfg.block_size)
-    dt = time.perf_counter() - t0
-    return rows / dt, dt
+    blk = max(1, -(-rows // (4 * threads)))
+    row_blocks = [(r0, min(rows, r0 + blk)) for r0 in range(0, rows, blk)]
+    normed = np.empty((L, rows, 8192), dtype=np.uint16)
+    kv = np.empty((L, rows, N), dtype=np.uint16)
+
+    def norms(rb):
+        r0, r1 = rb
+        normed[:, r0:r1] = oracle.context_norms(np.ascontiguousarray(x[r0:r1]), d["hidden_w"], d["pre_w"], L,
+                                                d["hidden_eps"], d["pre_eps"])
+
+    def project(task):
+        l, (r0, r1) = task
+        kv[l, r0:r1] = oracle.bf16(oracle.kv_project(normed[l:l + 1, r0:r1], d["w_kv"][l:l + 1])[0])
+
+    def store(task):
+        l, (r0, r1) = task
+        oracle.context_kv_store(kv[l:l + 1, r0:r1], H, pos[r0:r1], slots[l:l + 1, r0:r1], d["cos_sin"],
+                                caches[l:l + 1], cfg.block_size, d["k_eps"])
+
+    tasks = [(l, rb) for l in range(L) for rb in row_blocks]
+    times = {}
+    with ThreadPoolExecutor(threads) as ex:
+        for name, fn, work in (("norms", norms, row_blocks), ("projection", project, tasks),
+                               ("store", store, tasks)):
+            t0 = time.perf_counter()
+            list(ex.map(fn, work))
+            times[name] = time.perf_counter() - t0
+    return times
 
 
 def main():
@@ -99,7 +151,9 @@ def main():
     ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip timing the norm variants after the chain")
-    ap.add_argument("--cpu-rows", type=int, default=1536)
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of the workload the CPU oracle is timed on (the whole chain on those rows); "
+                         "default: every row, at most as many as hold the oracle's projection to 1.2 TFLOP")
     ap.add_argument("--path", choices=("fused", "unfused"), default="unfused")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device-to-device once, a known-size reference for HBM byte counters")
@@ -134,7 +188,7 @@ def main():
     w_kv = dv(d["w_kv"])
     cos_sin = None if d["cos_sin"] is None else dv(d["cos_sin"])
     positions = dv(d["positions"])
-    slots = dv(d["slots"])
+    slots = dv(d["slots"][0])  # the one slot mapping every layer shares
     fused = args.path == "fused"
     # Buffer sets the steps rotate over: a step whose touched bytes (rows in
     # and out, the projection weight, the written cache rows) fit twice in
@@ -216,7 +270,7 @@ def main():
     avg = {k: sum(v) / len(v) for k, v in k_ms.items()}
     log("per-kernel ms: " + ", ".join(f"{k}={v:.4f}" for k, v in avg.items()) + f"; wall/step {ms_step:.4f}")
 
-    norms_b, store_b, flops = algorithmic_bytes(cfg, d["slots"])
+    norms_b, store_b, flops = algorithmic_bytes(cfg, d["slots"][0])
     n0, n1, n2 = names
     if fused:
         # pre-pass: read x, write h and r (plus the hidden weight once)
@@ -324,14 +378,22 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        rows = min(args.cpu_rows, cfg.T)
+        per_row = 2 * cfg.L * 8192 * cfg.N  # projection flop per row, the oracle's dominant stage
+        rows = min(cfg.T, args.cpu_rows if args.cpu_rows > 0 else max(1, int(1.2e12 // per_row)))
+        threads, model = host_cpu()
         d["caches_host_sample"] = synth.random_bits_u16(cfg.stream(synth.TID_CACHE),
                                                        (cfg.L, cfg.num_blocks, cfg.H, cfg.block_size, 128))
-        log(f"cpu baseline: oracle chain on {rows} rows")
-        v, dt = cpu_baseline(d, cfg, rows)
-        cpu = {"value": v, "unit": "rows/s", "cores": 1, "kind": "oracle",
-               "sample": f"first {rows} of {cfg.T} rows of the {cfg.name} workload, whole chain "
-                         f"(norms, FP32 projection, store), single-threaded plain C, {dt:.1f} s"}
+        log(f"cpu baseline: oracle chain on {rows} rows, {threads} threads ({model}, nproc {os.cpu_count()})")
+        times = cpu_baseline(d, cfg, rows, threads)
+        total = sum(times.values())
+        what = "every row" if rows == cfg.T else f"the first {rows} of {cfg.T} rows"
+        cpu = {"value": rows / total, "unit": "rows/s", "cores": threads, "kind": "oracle",
+               "sample": f"{what} of the {cfg.name} workload, whole chain (norms, FP32 projection, store), "
+                         f"plain C oracle, each stage split over {threads} host threads, {total:.1f} s",
+               "cpu_model": model, "nproc": os.cpu_count(),
+               "stages_s": {k: round(v, 3) for k, v in times.items()},
+               "stages_rows_per_s": {k: rows / v for k, v in times.items()}}
+        log("cpu baseline: " + ", ".join(f"{k} {v:.2f} s" for k, v in times.items()))
 
     out = {
         "metric": "context rows/s (T=16K, L=4, D=8192); % HBM BW peak; bmm % MFMA peak",
