@@ -151,6 +151,8 @@ def main():
     ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip timing the norm variants after the chain")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip timing the norms against their traffic twin after the chain")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of the workload the CPU oracle is timed on (the whole chain on those rows); "
                          "default: every row, at most as many as hold the oracle's projection to 1.2 TFLOP")
@@ -347,6 +349,37 @@ def main():
             total += e0.elapsed_time(e1)
         return total / timed
 
+    # The ceiling of the norms' traffic: the norms kernel against its traffic
+    # twin (the same reads and writes in the same pattern and grid, no
+    # arithmetic) with the norms' streaming stores, with plain stores, and
+    # its reads and its writes alone; every launch cold, as in the chain.
+    ceiling = {}
+    if not args.no_ceiling:
+        flush_src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
+        twin_out = torch.empty((cfg.L, cfg.T, 8192), dtype=torch.bfloat16, device=dev)
+        staged = (1 if hw is not None else 0) + (cfg.L if pw is not None and cfg.L <= 8 else 0)
+        per_cu = 1 if staged * 16384 > 65536 else 2  # the norms' workgroups per CU
+        nb = cfg.T * 2 * 8192
+        runs = {
+            "context_norms": (lambda: nrc.context_norms(x, hw, pw, cfg.L, d["hidden_eps"], d["pre_eps"],
+                                                        out=twin_out), norms_b),
+            "twin, the norms' stores": (lambda: nrc.traffic_twin(x, cfg.L, nrc.TWIN_NORMS_STORES, twin_out, per_cu),
+                                        nb * (1 + cfg.L)),
+            "twin, plain stores": (lambda: nrc.traffic_twin(x, cfg.L, nrc.TWIN_PLAIN_STORES, twin_out, per_cu),
+                                   nb * (1 + cfg.L)),
+            "twin, reads only": (lambda: nrc.traffic_twin(x, cfg.L, nrc.TWIN_READS_ONLY, None, per_cu), nb),
+            "twin, writes only (the norms' stores)": (
+                lambda: nrc.traffic_twin(x, cfg.L, nrc.TWIN_WRITES_ONLY, twin_out, per_cu), nb * cfg.L),
+        }
+        for name, (run, nbytes) in runs.items():
+            ms = time_launches(run, flush_src)
+            ceiling[name] = {"ms": ms, "bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
+                             "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        ceiling["workgroups_per_cu"] = per_cu
+        del twin_out, flush_src
+        log("norms ceiling (cold): " + ", ".join(f"{k} {v['frac']:.3f}" for k, v in ceiling.items()
+                                                  if isinstance(v, dict)))
+
     variants = {}
     if not args.no_variants and hw is not None and pw is not None:
         flush_src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
@@ -420,6 +453,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "variants": variants,
+        "norms_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -386,6 +386,26 @@ int32_t nrc_check_scalars(const float* in, uint16_t* bf16_out, float* rsqrt_out,
  */
 int32_t nrc_check_bf16_pair(const float* in, uint16_t* out, int64_t n, void* stream);
 
+/*
+ * nrc_traffic_twin - diagnostic: the HBM traffic of nrc_context_norms
+ * without its arithmetic, to measure the bandwidth ceiling of that traffic.
+ * The same workgroups, grid, row walk and next-row prefetch as the norms
+ * kernel; each 256-thread row slot reads its row of x [T, 8192] bf16 in the
+ * norms' fragments (lane t: columns 2048 k + 8 t .. + 7, k < 4) and writes
+ * it unchanged to that row of each of the L outputs out [L, T, 8192].
+ *
+ *   mode    0: the norms' stores (non-temporal, system scope, buffer form);
+ *           1: plain stores; 2: reads only (out unused; each thread writes
+ *           one uint32 to sink); 3: writes only (x unused; a pattern)
+ *   per_cu  workgroups per CU at most: 1 as the norms with weights staged
+ *           past 64 KiB of LDS (the long workload), 2 otherwise
+ *   sink    mode 2: device uint32 array of at least per_cu * CUs * 1024
+ *           entries; else unused
+ * Errors: NRC_EINVAL (bad mode, per_cu, shape, NULL or misaligned operand).
+ */
+int32_t nrc_traffic_twin(const uint16_t* x, int64_t T, int32_t L, int32_t mode, int32_t per_cu, uint16_t* out,
+                         uint32_t* sink, int64_t sink_len, void* stream);
+
 /* Thread-local description of the last non-zero status of this thread. */
 const char* nrc_last_error(void);
 

@@ -109,6 +109,8 @@ def _load():
     L.nrc_context_kv_project_fused.argtypes = [_vp, _vp, _vp, _f32, _vp, _vp, _i32, _i64, _i64, _i64, _vp]
     L.nrc_check_scalars.restype = _i32
     L.nrc_check_scalars.argtypes = [_vp, _vp, _vp, _i64, _vp]
+    L.nrc_traffic_twin.restype = _i32
+    L.nrc_traffic_twin.argtypes = [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _i64, _vp]
     L.nrc_check_bf16_pair.restype = _i32
     L.nrc_check_bf16_pair.argtypes = [_vp, _vp, _i64, _vp]
     _lib = L
@@ -646,6 +648,35 @@ def check_bf16_pair(x, stream=None):
         raise TypeError("x must be a contiguous float32 GPU tensor")
     out = torch.empty(x.shape, dtype=torch.int16, device=x.device)
     _check(_load().nrc_check_bf16_pair(_ptr(x), _ptr(out), x.numel(), _stream(stream)))
+    return out
+
+
+TWIN_NORMS_STORES, TWIN_PLAIN_STORES, TWIN_READS_ONLY, TWIN_WRITES_ONLY = 0, 1, 2, 3
+
+
+def traffic_twin(x, L, mode, out=None, per_cu=1, stream=None):
+    """Diagnostic: the norms' HBM traffic (read x [T, 8192], write it to L
+    rows of out [L, T, 8192]) in the norms' access pattern, no arithmetic;
+    mode TWIN_* as in nrc.h. Returns out."""
+    import torch
+
+    _bf16(x, "x")
+    T = x.shape[0]
+    if tuple(x.shape) != (T, HIDDEN):
+        raise ValueError("x must be [T, 8192]")
+    if out is None and mode != TWIN_READS_ONLY:
+        out = torch.empty((L, T, HIDDEN), dtype=torch.bfloat16, device=x.device)
+    if out is not None:
+        _bf16(out, "out")
+        _same_device(out, x, "out")
+        if tuple(out.shape) != (L, T, HIDDEN):
+            raise ValueError("out must be [L, T, 8192]")
+    sink = None
+    if mode == TWIN_READS_ONLY:
+        n = per_cu * torch.cuda.get_device_properties(x.device).multi_processor_count * 1024
+        sink = torch.empty(n, dtype=torch.int32, device=x.device)
+    _check(_load().nrc_traffic_twin(_ptr(x), T, L, mode, per_cu, _ptr(out), _ptr(sink),
+                                    0 if sink is None else sink.numel(), _stream(stream)))
     return out
 
 

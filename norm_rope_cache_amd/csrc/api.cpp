@@ -460,4 +460,22 @@ int32_t nrc_check_bf16_pair(const float* in, uint16_t* out, int64_t n, void* str
     return launch_status(nrc::launch_bf16_pair(in, out, n, (hipStream_t)stream), "check_bf16_pair");
 }
 
+
+int32_t nrc_traffic_twin(const uint16_t* x, int64_t T, int32_t L, int32_t mode, int32_t per_cu, uint16_t* out,
+                         uint32_t* sink, int64_t sink_len, void* stream) {
+    if (mode < 0 || mode > 3) return fail(NRC_EINVAL, "traffic_twin: mode %d (0..3)", mode);
+    if (per_cu != 1 && per_cu != 2) return fail(NRC_EINVAL, "traffic_twin: per_cu %d (1 or 2)", per_cu);
+    if (T < 0 || L < 1 || T > ((int64_t)1 << 31)) return fail(NRC_EINVAL, "traffic_twin: T = %lld, L = %d", (long long)T, L);
+    if (T == 0) return NRC_OK;
+    if ((mode != 3 && !x) || (mode != 2 && !out)) return fail(NRC_EINVAL, "traffic_twin: NULL operand");
+    const int cus = num_cus();
+    if (mode == 2 && (!sink || sink_len < (int64_t)per_cu * cus * 1024))
+        return fail(NRC_EINVAL, "traffic_twin: the reads-only mode needs a sink of %lld uint32",
+                    (long long)((int64_t)per_cu * cus * 1024));
+    if ((x && !aligned(x, 16)) || (out && !aligned(out, 16)))
+        return fail(NRC_EINVAL, "traffic_twin: operands must be 16-byte aligned");
+    return launch_status(nrc::launch_traffic_twin(x, T, L, mode, per_cu, out, sink, cus, (hipStream_t)stream),
+                         "traffic_twin");
+}
+
 }  // extern "C"

@@ -137,6 +137,11 @@ int launch_kv_project_fused(const ProjectArgs& a, const float* r, const uint16_t
                             hipStream_t stream);
 
 int launch_bf16_pair(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
+// The norms' traffic without their arithmetic (selftest.hip): mode 0 the
+// norms' stores, 1 plain stores, 2 reads only (one dword per thread to sink),
+// 3 writes only; per_cu workgroups per CU at most.
+int launch_traffic_twin(const uint16_t* x, int64_t T, int32_t L, int32_t mode, int32_t per_cu, uint16_t* out,
+                        uint32_t* sink, int32_t num_cus, hipStream_t stream);
 int launch_scalars(const float* in, uint16_t* bf, float* rs, int64_t n, hipStream_t stream);
 
 }  // namespace nrc
