@@ -17,9 +17,13 @@
 //   - A fragments are read with ds_read_b128 (8 consecutive k of one row),
 //     B fragments with ds_read_b64_tr_b16, which transposes the N-contiguous
 //     B tile into the k-contiguous operand layout on the fly;
-//   - XOR swizzles on 16-byte chunks (A: chunk ^ ((row >> 2) & 3), B: chunk
-//     ^ (4 (k-row & 3) ^ ((k-row >> 3) & 3))) spread every fragment read over
-//     the 64 LDS banks;
+//   - XOR swizzles on 16-byte chunks make every fragment read free of LDS
+//     bank conflicts (the SQ_LDS_BANK_CONFLICT counter reads 0): A rows XOR
+//     bits (r1 ^ r2, r2 ^ r3) of the row into the chunk index, so that each
+//     16 lanes of a 16-byte read (and each 8) hit distinct 16-byte bank
+//     groups; B k-rows XOR 2 (k & 3) and 8 ((k >> 3) & 1), so that the 32
+//     lanes of an 8-byte transposing read (and each 16) do the same - the
+//     k-row group must not touch chunk bit 0, which the column pair sets;
 //   - the loop is scheduled by hand (reads and DMA between consecutive
 //     MFMAs, sched_barrier fences): while stage st is multiplied, the
 //     fragments of stage st + 1 are read and the DMA of stage st + 3 goes
@@ -54,9 +58,11 @@ typedef __attribute__((address_space(3))) u32x4v lds_u32x4;
 constexpr int kBK = 32;     // K per LDS stage
 constexpr int kStages = 4;  // LDS ring depth
 
-// 16-byte chunk swizzles of the LDS tiles (see the header).
-__device__ __forceinline__ int swz_a(int row) { return (row >> 2) & 3; }
-__device__ __forceinline__ int swz_b(int krow) { return (4 * (krow & 3)) ^ ((krow >> 3) & 3); }
+// 16-byte chunk swizzles of the LDS tiles (see the header). swz_a depends on
+// bits 1..3 of the row only, so every A chunk a lane's DMA writes (rows 16
+// apart) sits at the same k chunk.
+__device__ __forceinline__ int swz_a(int row) { return (((row >> 1) ^ (row >> 2)) & 1) | ((((row >> 2) ^ (row >> 3)) & 1) << 1); }
+__device__ __forceinline__ int swz_b(int krow) { return (2 * (krow & 3)) ^ (8 * ((krow >> 3) & 1)); }
 
 template <int BM, int BN, int WM, int WN>
 struct Cfg {
@@ -349,9 +355,13 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
             bfr[f][j] = __builtin_bit_cast(bf16x8, nxt);
         }
     };
+    // The weight fragment goes in as the MFMA's first operand: the block is
+    // computed transposed, so that each lane ends with four consecutive
+    // columns of one row (16 x 16 block: lane l holds row l % 16, columns
+    // 4 (l / 16) .. 4 (l / 16) + 3) and the epilogue stores them together.
     auto mfma_one = [&](int f, int idx) {
         const int i = idx / CF::NI, j = idx % CF::NI;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[f][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[f][j], af[i], acc[i][j], 0, 0, 0);
     };
     const int nk = (int)(k_len / kBK);
     // DMA d (0 .. LOADS-1: A blocks, then B blocks) of stage st into buffer
@@ -403,32 +413,56 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
     set_sources();
     set_fused();
     issue_prologue();
-    // Epilogue: lane holds column (lane & 15) of each 16 x 16 block, rows
-    // 4 (lane / 16) + v, v < 4.
+    // Epilogue: lane holds row (lane & 15) of each 16 x 16 block, columns
+    // 4 (lane / 16) + v, v < 4: one 8-byte store of bf16 (16 bytes of FP32
+    // partial sums) per block. Rounding: the paired hardware conversion
+    // (nearest even, the library's rounding for every non-NaN value) when no
+    // sum of the wave's tile is NaN, else the exact bit-pattern rounding
+    // (NaN -> 0x7FC0).
     auto epilogue = [&](int e_layer, int64_t e_m0, int64_t e_n0, int e_ks) {
     uint16_t* Cl = C + (int64_t)e_layer * M * N;
     float* Wl = W + ((int64_t)e_ks * L + e_layer) * M * N;
-    auto store_tile = [&](auto checked) {
+    bool nan = false;
+    if constexpr (!SPLIT) {
 #pragma unroll
         for (int i = 0; i < CF::MI; ++i)
 #pragma unroll
-            for (int j = 0; j < CF::NI; ++j) {
-                const int64_t col = e_n0 + wn * CF::WTN + 16 * j + (lane & 15);
+            for (int j = 0; j < CF::NI; ++j)
+                nan = nan || __builtin_isunordered(acc[i][j][0], acc[i][j][1]) ||
+                      __builtin_isunordered(acc[i][j][2], acc[i][j][3]);
+    }
+    auto store_tile = [&](auto checked, auto exact) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int64_t row = e_m0 + wm * CF::WTM + 16 * i + 4 * (lane >> 4) + v;
-                    if (decltype(checked)::value && row >= M) continue;
-                    if constexpr (SPLIT)
-                        Wl[row * N + col] = acc[i][j][v];
-                    else
-                        Cl[row * N + col] = (uint16_t)to_bf16(acc[i][j][v]);
+        for (int i = 0; i < CF::MI; ++i) {
+            const int64_t row = e_m0 + wm * CF::WTM + 16 * i + (lane & 15);
+            if (decltype(checked)::value && row >= M) continue;
+#pragma unroll
+            for (int j = 0; j < CF::NI; ++j) {
+                const int64_t col = e_n0 + wn * CF::WTN + 16 * j + 4 * (lane >> 4);
+                const f32x4 c = acc[i][j];
+                if constexpr (SPLIT) {
+                    *reinterpret_cast<f32x4*>(Wl + row * N + col) = c;
+                } else if constexpr (decltype(exact)::value) {
+                    *reinterpret_cast<uint2*>(Cl + row * N + col) = uint2{pack_bf16(c[0], c[1]), pack_bf16(c[2], c[3])};
+                } else {
+                    *reinterpret_cast<uint2*>(Cl + row * N + col) =
+                        uint2{pack_bf16_pair_hw(c[0], c[1]), pack_bf16_pair_hw(c[2], c[3])};
                 }
             }
+        }
     };
-    if (e_m0 + BM <= M)
-        store_tile(std::false_type{});
-    else
-        store_tile(std::true_type{});
+    const bool full = e_m0 + BM <= M;
+    if (__builtin_amdgcn_ballot_w64(nan) != 0) {
+        if (full)
+            store_tile(std::false_type{}, std::true_type{});
+        else
+            store_tile(std::true_type{}, std::true_type{});
+    } else {
+        if (full)
+            store_tile(std::false_type{}, std::false_type{});
+        else
+            store_tile(std::true_type{}, std::false_type{});
+    }
     };
 
     // Slots of the schedule (MFMA index after which a piece is issued).
