@@ -295,6 +295,26 @@ int32_t nrc_context_kv_project_fused(const uint16_t* h, const float* r, const ui
                                      void* stream);
 
 /*
+ * nrc_context_kv_project_fused_split - nrc_context_kv_project_fused that
+ * splits the summation axis for shapes with few output tiles (small T), as
+ * nrc_context_kv_project_split does: the same slices, the same fixed-order
+ * addition, so the same bits as nrc_context_kv_project_split on the stacked
+ * layer norms. Page "...runtime.draft", ContextKV._project (a stock bmm,
+ * summation order free) on the norms of "...cutedsl.draft.context",
+ * _ContextNormsKernel.
+ *
+ *   workspace, workspace_bytes  as nrc_context_kv_project_split: caller-owned
+ *                    device memory of nrc_context_kv_project_workspace_bytes(L,
+ *                    T, D, N) bytes, 16-byte aligned; unused when that is 0.
+ *   Other arguments and errors as nrc_context_kv_project_fused, plus
+ *   NRC_EINVAL for a workspace that is NULL, too small or misaligned when
+ *   the shape splits. Calls that share a workspace must not overlap.
+ */
+int32_t nrc_context_kv_project_fused_split(const uint16_t* h, const float* r, const uint16_t* pre_w, float pre_center,
+                                           const uint16_t* w, uint16_t* kv, int32_t L, int64_t T, int64_t D,
+                                           int64_t N, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * nrc_context_kv_store - weightless K-norm, GPT-J RoPE and paged-cache insert
  * of L layers. Page "...cutedsl.draft.context", sections ContextKvStore,
  * _ContextKvStoreKernel, _sum_squares_64 and _rope; operand checks per

@@ -107,6 +107,9 @@ def _load():
     L.nrc_context_hidden_norm.argtypes = [_vp, _i64, _i64, _vp, _vp, _i32, _f32, _f32, _f32, _f32, _vp, _vp, _vp]
     L.nrc_context_kv_project_fused.restype = _i32
     L.nrc_context_kv_project_fused.argtypes = [_vp, _vp, _vp, _f32, _vp, _vp, _i32, _i64, _i64, _i64, _vp]
+    L.nrc_context_kv_project_fused_split.restype = _i32
+    L.nrc_context_kv_project_fused_split.argtypes = [_vp, _vp, _vp, _f32, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i64,
+                                                     _vp]
     L.nrc_check_scalars.restype = _i32
     L.nrc_check_scalars.argtypes = [_vp, _vp, _vp, _i64, _vp]
     L.nrc_traffic_twin.restype = _i32
@@ -315,9 +318,11 @@ def context_hidden_norm(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hi
     return h, r
 
 
-def context_kv_project_fused(h, r, pre_w, w_kv, pre_center=0.0, out=None, stream=None):
+def context_kv_project_fused(h, r, pre_w, w_kv, pre_center=0.0, out=None, stream=None, split=True):
     """kv[l] = bf16((h * |r|) * (pre_w[l] + pre_center)) . w_kv[l]; equal to
-    context_norms followed by context_kv_project."""
+    context_norms followed by context_kv_project with the same `split`
+    (small T: the summation split over several workgroups, with a workspace
+    from torch's allocator; split=False keeps the one-pass kernel)."""
     import torch
 
     _bf16(h, "h")
@@ -343,8 +348,19 @@ def context_kv_project_fused(h, r, pre_w, w_kv, pre_center=0.0, out=None, stream
         _same_device(out, h, "out")
         if tuple(out.shape) != (L, T, N):
             raise ValueError("out must be [L, T, N]")
-    _check(_load().nrc_context_kv_project_fused(_ptr(h), _ptr(r), _ptr(pre_w), pre_center, _ptr(w_kv), _ptr(out), L,
-                                                T, D, N, _stream(stream)))
+    lib = _load()
+    need = lib.nrc_context_kv_project_workspace_bytes(L, T, D, N) if split else 0
+    if need < 0:
+        _check(need)
+    if need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=h.device)
+        if stream is not None:
+            ws.record_stream(stream)  # the allocator may reuse it only after this stream's work
+        _check(lib.nrc_context_kv_project_fused_split(_ptr(h), _ptr(r), _ptr(pre_w), pre_center, _ptr(w_kv), _ptr(out),
+                                                      L, T, D, N, _ptr(ws), need, _stream(stream)))
+    else:
+        _check(lib.nrc_context_kv_project_fused(_ptr(h), _ptr(r), _ptr(pre_w), pre_center, _ptr(w_kv), _ptr(out), L,
+                                                    T, D, N, _stream(stream)))
     return out
 
 
@@ -687,15 +703,15 @@ def context_kv_chain(x, hidden_w, pre_w, w_kv, positions, slots, cos_sin, caches
     fused=False (the faster form on MI355X): norms into `workspace`
     ([L, T, 8192] bf16) -> projection -> store. fused=True: pre-pass (h, r)
     -> fused projection -> store, without the [L, T, 8192] intermediate;
-    `workspace` may be a tuple (h [T, 8192] bf16, r [T] float32). Both write
-    the same bits when the unfused projection runs in one pass (split=False);
-    for small T it otherwise splits the summation (see context_kv_project),
-    which changes the rounding within the projection's tolerance."""
+    `workspace` may be a tuple (h [T, 8192] bf16, r [T] float32). Both forms
+    write the same bits for the same `split`; for small T split=True splits
+    the summation (see context_kv_project), which changes the rounding
+    within the projection's tolerance."""
     L = w_kv.shape[0]
     if fused:
         h, r = workspace if workspace is not None else (None, None)
         h, r = context_hidden_norm(x, hidden_w, pre_w, L, hidden_eps, pre_eps, h=h, r=r, stream=stream)
-        kv = context_kv_project_fused(h, r, pre_w, w_kv, out=kv, stream=stream)
+        kv = context_kv_project_fused(h, r, pre_w, w_kv, out=kv, stream=stream, split=split)
     else:
         normed = context_norms(x, hidden_w, pre_w, L, hidden_eps, pre_eps, out=workspace, stream=stream)
         kv = context_kv_project(normed, w_kv, out=kv, stream=stream, split=split)

@@ -160,9 +160,13 @@ int32_t nrc_context_hidden_norm(const uint16_t* x, int64_t T, int64_t D, const u
     return launch_status(nrc::launch_hidden_norm(a, h, r, (hipStream_t)stream), "context_hidden_norm");
 }
 
-int32_t nrc_context_kv_project_fused(const uint16_t* h, const float* r, const uint16_t* pre_w, float pre_center,
-                                     const uint16_t* w, uint16_t* kv, int32_t L, int64_t T, int64_t D, int64_t N,
-                                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of the fused projection's operands (both entry points).
+int32_t fused_checks(const uint16_t* h, const float* r, const uint16_t* pre_w, const uint16_t* w, const uint16_t* kv,
+                     int32_t L, int64_t T, int64_t D, int64_t N) {
     if (L < 1) return fail(NRC_EINVAL, "context_kv_project_fused: L = %d < 1", L);
     if (T < 0) return fail(NRC_EINVAL, "context_kv_project_fused: T = %lld < 0", (long long)T);
     if (D != NRC_HIDDEN)
@@ -176,6 +180,18 @@ int32_t nrc_context_kv_project_fused(const uint16_t* h, const float* r, const ui
     if (!h || !r || !w || !kv) return fail(NRC_EINVAL, "context_kv_project_fused: NULL operand");
     if (!aligned(h, 16) || !aligned(w, 16) || !aligned(kv, 16) || !aligned(r, 4) || (pre_w && !aligned(pre_w, 16)))
         return fail(NRC_EINVAL, "context_kv_project_fused: operands must be 16-byte aligned (r 4-byte)");
+    return NRC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t nrc_context_kv_project_fused(const uint16_t* h, const float* r, const uint16_t* pre_w, float pre_center,
+                                     const uint16_t* w, uint16_t* kv, int32_t L, int64_t T, int64_t D, int64_t N,
+                                     void* stream) {
+    if (int32_t rc = fused_checks(h, r, pre_w, w, kv, L, T, D, N)) return rc;
+    if (T == 0) return NRC_OK;
     nrc::ProjectArgs a{h, w, kv, L, T, D, N, num_cus()};
     return launch_status(nrc::launch_kv_project_fused(a, r, pre_w, pre_center, (hipStream_t)stream),
                          "context_kv_project_fused");
@@ -249,6 +265,24 @@ int32_t nrc_context_kv_project_split(const uint16_t* normed, const uint16_t* w, 
                                      int32_t L, int64_t T, int64_t D, int64_t N, void* workspace,
                                      int64_t workspace_bytes, void* stream) {
     return project_impl(normed, w, w_layout, kv, L, T, D, N, workspace, workspace_bytes, true, stream);
+}
+
+int32_t nrc_context_kv_project_fused_split(const uint16_t* h, const float* r, const uint16_t* pre_w, float pre_center,
+                                           const uint16_t* w, uint16_t* kv, int32_t L, int64_t T, int64_t D,
+                                           int64_t N, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (int32_t rc = fused_checks(h, r, pre_w, w, kv, L, T, D, N)) return rc;
+    if (T == 0) return NRC_OK;
+    nrc::ProjectArgs a{h, w, kv, L, T, D, N, num_cus()};
+    const int64_t need = project_workspace_bytes(L, T, D, N);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
+            return fail(NRC_EINVAL, "context_kv_project_fused_split: needs a 16-byte aligned workspace of %lld bytes",
+                        (long long)need);
+        a.ws = static_cast<float*>(workspace);
+        a.k_split = nrc::kv_project_k_split(L, T, D, N, a.num_cus);
+    }
+    return launch_status(nrc::launch_kv_project_fused(a, r, pre_w, pre_center, (hipStream_t)stream),
+                         "context_kv_project_fused_split");
 }
 
 static_assert(NRC_PROJECT_SCRATCH_BYTES == nrc::kProjectScratchBytes, "header and library scratch sizes differ");

@@ -639,6 +639,22 @@ def test_project_several_tiles_per_workgroup(nrc, oracle, L, T, N):
     _project_check(nrc, oracle, A, B, rows, f"project multi-tile L={L} T={T} N={N}")
 
 
+@pytest.mark.parametrize("L,T,N,split", [(5, 2000, 2048, False), (5, 300, 2048, False), (5, 300, 2048, True)])
+def test_project_weights_beyond_half_the_infinity_cache(nrc, oracle, L, T, N, split):
+    """Stacked weights over 128 MB take the layer-synchronous tile order:
+    320 tiles of 256 x 256 over 256 workgroups (a ragged last round on two
+    XCDs and a ragged last row tile), 128 x 128 tiles in one pass, and the
+    split form; sampled rows against the oracle."""
+    from norm_rope_cache_amd import synth
+
+    assert L * 8192 * N * 2 > (128 << 20)
+    A = synth.normal_bf16(8100 + T, (L, T, 8192))
+    B = synth.normal_bf16(8200 + N, (L, 8192, N), std=0.02)
+    rows = np.unique(np.concatenate([[0, T - 1], np.arange(1, T, max(1, T // 24))]))
+    _say(f"project large weights L={L} T={T} N={N} split={split}")
+    _project_check(nrc, oracle, A, B, rows, f"project large weights {L},{T},{N}", split=split)
+
+
 @pytest.mark.parametrize("L,T,N", [(2, 37, 256), (4, 300, 1024), (1, 513, 384), (4, 16384, 1024)])
 def test_project_nd_weight_layout(nrc, oracle, L, T, N):
     """The pages' [L, N, D] weight storage: the same bits as the [L, D, N]
@@ -1162,14 +1178,16 @@ def test_hidden_norm_parity_configs(nrc, oracle, name):
     assert same.all(), f"hidden norm r {name}: {np.nonzero(~same)[0][:5]}"
 
 
-def _fused_vs_unfused(nrc, x, hw, pw, w_kv, L, he=1e-6, pe=1e-6, hc=0.0, pc=0.0):
+def _fused_vs_unfused(nrc, x, hw, pw, w_kv, L, he=1e-6, pe=1e-6, hc=0.0, pc=0.0, split=False):
+    """(unfused kv, fused kv), both in one pass (split=False) or both with
+    the summation split where the shape splits (split=True)."""
     xd, wd = to_dev(x), to_dev(w_kv)
     hwd = None if hw is None else to_dev(hw)
     pwd = None if pw is None else to_dev(pw)
     normed = nrc.context_norms(xd, hwd, pwd, L, he, pe, hc, pc)
-    kv_u = nrc.context_kv_project(normed, wd, split=False)  # one pass, like the fused kernel
+    kv_u = nrc.context_kv_project(normed, wd, split=split)
     h, r = nrc.context_hidden_norm(xd, hwd, pwd, L, he, pe, hc, pc)
-    kv_f = nrc.context_kv_project_fused(h, r, pwd, wd, pc)
+    kv_f = nrc.context_kv_project_fused(h, r, pwd, wd, pc, split=split)
     torch.cuda.synchronize()
     return to_host(kv_u), to_host(kv_f)
 
@@ -1194,6 +1212,53 @@ def test_fused_project_parity_configs(nrc, oracle, name):
     on = oracle.context_norms(np.ascontiguousarray(d["x"][rows]), d["hidden_w"], d["pre_w"], cfg.L)
     ok, msg = projection_tolerance_ok(kv_f[:, rows], oracle.kv_project(on, d["w_kv"]))
     assert ok, f"fused {name}: {msg}"
+
+
+@pytest.mark.parametrize("L,T,N", [(4, 512, 1024), (2, 16, 128), (2, 300, 384), (3, 700, 512), (4, 256, 1024)])
+def test_fused_split_matches_unfused_split(nrc, oracle, L, T, N):
+    """The fused projection with its summation split (small T) equals the
+    unfused split projection on the stacked norms bit for bit - the same
+    slices and the same fixed-order addition - for 256 x 256 and 128 x 128
+    slices, and is within tolerance of the oracle on sampled rows."""
+    from norm_rope_cache_amd import synth
+
+    lib = nrc._load()
+    assert lib.nrc_context_kv_project_workspace_bytes(L, T, 8192, N) > 0, "shape should split"
+    x = synth.normal_bf16(7401 + T, (T, 8192))
+    hw = synth.normal_bf16(7402, (8192,), 1.0, 0.3)
+    pw = synth.normal_bf16(7403, (L, 8192), 1.0, 0.3)
+    w = synth.normal_bf16(7404 + N, (L, 8192, N), std=0.02)
+    _say(f"fused split L={L} T={T} N={N}")
+    kv_u, kv_f = _fused_vs_unfused(nrc, x, hw, pw, w, L, split=True)
+    assert_bits_equal(kv_f, kv_u, f"fused split vs unfused split {L},{T},{N}")
+    rows = np.unique(np.concatenate([[0, T - 1], np.arange(1, T, max(1, T // 20))]))
+    on = oracle.context_norms(np.ascontiguousarray(x[rows]), hw, pw, L)
+    ok, msg = projection_tolerance_ok(kv_f[:, rows], oracle.kv_project(on, w))
+    assert ok, f"fused split {L},{T},{N}: {msg}"
+
+
+def test_fused_split_special_values(nrc):
+    """NaN / Inf / overflow / zero rows, -0.0 and NaN layer weights, non-zero
+    centers, weightless layer norms: the fused split equals the unfused
+    split bit for bit."""
+    from norm_rope_cache_amd import synth
+
+    T, L, N = 300, 3, 256
+    x = synth.edge_mixture_bf16(191, 192, (T, 8192), nan_inf=True)
+    x[3] = 0
+    x[4] = 0x8000
+    x[6, :] = 0x7F7F
+    x[7:40] = synth.normal_bf16(194, (33, 8192))
+    hw = synth.normal_bf16(195, (8192,), 1.0, 0.3)
+    pw = synth.normal_bf16(196, (L, 8192), 1.0, 0.3)
+    pw[:, ::83] = 0x8000
+    pw_nan = pw.copy()
+    pw_nan[2, 4000] = 0x7FC1
+    w = synth.normal_bf16(197, (L, 8192, N), std=0.02)
+    for pre_w, hc, pc in [(pw, 0.0, 0.0), (None, 0.0, 0.0), (pw, 0.5, -0.25), (pw_nan, 0.0, 0.0)]:
+        _say(f"fused split specials pre_w={'yes' if pre_w is not None else 'no'} centers={hc},{pc}")
+        kv_u, kv_f = _fused_vs_unfused(nrc, x, hw, pre_w, w, L, 1e-6, 1e-6, hc, pc, split=True)
+        assert_bits_equal(kv_f, kv_u, f"fused split vs unfused split specials {hc},{pc}")
 
 
 def test_fused_project_layer_changes_within_a_workgroup(nrc):
