@@ -157,6 +157,9 @@ def main():
                     help="rows of the workload the CPU oracle is timed on (the whole chain on those rows); "
                          "default: every row, at most as many as hold the oracle's projection to 1.2 TFLOP")
     ap.add_argument("--path", choices=("fused", "unfused"), default="unfused")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="KV heads to project and store (default: the workload's); e.g. 1 for the long workload's "
+                         "per-GPU share under 8-way tensor parallelism, which splits the heads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device-to-device once, a known-size reference for HBM byte counters")
     args = ap.parse_args()
@@ -174,6 +177,10 @@ def main():
     from norm_rope_cache_amd import synth
 
     cfg = synth.CONFIGS[args.workload]
+    if args.kv_heads:
+        from dataclasses import replace
+
+        cfg = replace(cfg, H=args.kv_heads)
     log(f"generating {cfg.name}: L={cfg.L} T={cfg.T} H={cfg.H}")
     d = synth.make_inputs(cfg, with_cache=False)
     dev = torch.device("cuda", 0)
