@@ -22,12 +22,12 @@
 //     B fragments with ds_read_b64_tr_b16, which transposes the N-contiguous
 //     B tile into the k-contiguous operand layout on the fly;
 //   - XOR swizzles on 16-byte chunks make every fragment read free of LDS
-//     bank conflicts (the SQ_LDS_BANK_CONFLICT counter reads 0): A rows XOR
-//     bits (r1 ^ r2, r2 ^ r3) of the row into the chunk index, so that each
-//     16 lanes of a 16-byte read (and each 8) hit distinct 16-byte bank
-//     groups; B k-rows XOR 2 (k & 3) and 8 ((k >> 3) & 1), so that the 32
-//     lanes of an 8-byte transposing read (and each 16) do the same - the
-//     k-row group must not touch chunk bit 0, which the column pair sets;
+//     bank conflicts (the SQ_LDS_BANK_CONFLICT counter reads 0): B k-rows
+//     XOR 2 (k & 3) and 8 ((k >> 3) & 1), so that the lanes of an 8-byte
+//     transposing read hit distinct bank groups (the k-row group must not
+//     touch chunk bit 0, which the column pair sets); A rows of a stage pair
+//     XOR r & 7 (per-stage A rows, in the fused form, bits (r1 ^ r2, r2 ^
+//     r3) of the row);
 //   - the loop is scheduled by hand (reads and DMA between consecutive
 //     MFMAs, sched_barrier fences): while stage st is multiplied, the
 //     fragments of stage st + 1 are read and the DMA of stage st + 3 goes
@@ -67,9 +67,11 @@ constexpr int kStages = 4;  // LDS ring depth
 // apart) sits at the same k chunk.
 __device__ __forceinline__ int swz_a(int row) { return (((row >> 1) ^ (row >> 2)) & 1) | ((((row >> 2) ^ (row >> 3)) & 1) << 1); }
 __device__ __forceinline__ int swz_b(int krow) { return (2 * (krow & 3)) ^ (8 * ((krow >> 3) & 1)); }
-// A rows of a stage pair (64 k, 128 bytes = 8 chunks): chunk ^ ((r & 7) ^
-// ((r >> 3) & 1)); free of bank conflicts for the stage-pair layout below.
-__device__ __forceinline__ int swz_a2(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// A rows of a stage pair (64 k, 128 bytes = 8 chunks): chunk ^ (r & 7).
+// Chosen by the SQ_LDS_BANK_CONFLICT counter, which reads 0 with it; a
+// swizzle that also XORed row bit 3 (conflict-free by a 64-bank, 16-lanes-
+// per-cycle model of the reads) read 2 conflict cycles per LDS instruction.
+__device__ __forceinline__ int swz_a2(int row) { return row & 7; }
 
 template <int BM, int BN, int WM, int WN>
 struct Cfg {
