@@ -11,9 +11,15 @@ H=8 KV heads, RoPE table [131072, 64], block size 16, 8192 blocks).
 
     python bench.py [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
 
-Prints ONE JSON line on stdout; progress goes to stderr. Per-kernel launch
-durations come from HIP events recorded on the stream the kernels run on
-(torch's current stream, which the binding passes to every call).
+Prints ONE JSON line on stdout; progress goes to stderr. Launch durations
+come from HIP events recorded on the stream the kernels run on (torch's
+current stream, which the binding passes to every call), created as timing
+events (hipEventDisableSystemFence: recording one does not write back and
+invalidate the caches at system scope, which with default events costs each
+event a few microseconds of stall and leaves the next kernel cold). The timed
+region records events only around the dominant kernel (two per step); the
+per-kernel figures come from a pass of as many steps with events between all
+calls, run before it.
 """
 
 import argparse
@@ -32,6 +38,60 @@ PEAK_CLOCK_GHZ = 2.4           # the engine clock the MFMA peak is quoted at
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+class HipTimer:
+    """HIP events for timing only, from the HIP runtime this process has
+    loaded (the one torch and libnrc share), created with
+    hipEventDisableSystemFence and recorded on torch's current stream."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded in this process")
+        self._ct = ctypes
+        self._hip = h = ctypes.CDLL(path)
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._events = []
+
+    def event(self):
+        e = self._ct.c_void_p()
+        rc = self._hip.hipEventCreateWithFlags(self._ct.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self._events.append(e)
+        return e
+
+    def record(self, e):
+        import torch
+
+        rc = self._hip.hipEventRecord(e, self._ct.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, e0, e1):
+        f = self._ct.c_float()
+        rc = self._hip.hipEventElapsedTime(self._ct.byref(f), e0, e1)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return f.value
+
+    def close(self):
+        for e in self._events:
+            self._hip.hipEventDestroy(e)
+        self._events = []
 
 
 def algorithmic_bytes(cfg, slots_np):
@@ -227,27 +287,37 @@ def main():
              ["context_norms", "context_kv_project", "context_kv_store"])
 
     step_no = [0]
+    nrc._load()
+    timer = HipTimer()
 
-    def step(ev=None):
+    def step(ev=None, around=None):
+        """One chain step. ev: four events recorded between the calls (the
+        per-kernel pass); around: (call index, event, event) recorded just
+        before and after that one call (the timed region)."""
         b = sets[step_no[0] % n_sets]
         step_no[0] += 1
-        if ev:
-            ev[0].record()
+
+        def mark(i):
+            if ev:
+                timer.record(ev[i])
+            if around and around[0] == i:
+                timer.record(around[1])
+            if around and around[0] + 1 == i:
+                timer.record(around[2])
+
+        mark(0)
         if fused:
             nrc.context_hidden_norm(b["x"], hw, pw, cfg.L, d["hidden_eps"], d["pre_eps"], h=b["h"], r=b["r"])
         else:
             nrc.context_norms(b["x"], hw, pw, cfg.L, d["hidden_eps"], d["pre_eps"], out=b["normed"])
-        if ev:
-            ev[1].record()
+        mark(1)
         if fused:
             nrc.context_kv_project_fused(b["h"], b["r"], pw, b["w"], out=b["kv"])
         else:
             nrc.context_kv_project(b["normed"], b["w"], out=b["kv"])
-        if ev:
-            ev[2].record()
+        mark(2)
         nrc.context_kv_store(b["kv"], positions, slots, cos_sin, b["caches"], cfg.H, d["k_eps"])
-        if ev:
-            ev[3].record()
+        mark(3)
 
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev).random_(-32768, 32767)
@@ -263,21 +333,35 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    log(f"timing {args.steps} steps")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    # Per-kernel pass: as many steps as the timed region, events between all
+    # calls; its durations give each kernel's figures and pick the dominant
+    # kernel (the longest launch).
+    log(f"per-kernel pass: {args.steps} steps")
+    events = [[timer.event() for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
     k_ms = {n: [] for n in names}
     for ev in events:
         for i, n in enumerate(names):
-            k_ms[n].append(ev[i].elapsed_time(ev[i + 1]))
+            k_ms[n].append(timer.elapsed_ms(ev[i], ev[i + 1]))
     avg = {k: sum(v) / len(v) for k, v in k_ms.items()}
-    log("per-kernel ms: " + ", ".join(f"{k}={v:.4f}" for k, v in avg.items()) + f"; wall/step {ms_step:.4f}")
+    dom = max(avg, key=avg.get)
+    dom_i = names.index(dom)
+
+    # Timed region: K steps, events only around the dominant kernel's call.
+    log(f"timing {args.steps} steps")
+    around = [(dom_i, timer.event(), timer.event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(around=around[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    dom_ms = sum(timer.elapsed_ms(a[1], a[2]) for a in around) / args.steps
+    log("per-kernel ms (per-kernel pass): " + ", ".join(f"{k}={v:.4f}" for k, v in avg.items()) +
+        f"; timed region: wall/step {ms_step:.4f}, {dom} {dom_ms:.4f}")
 
     norms_b, store_b, flops = algorithmic_bytes(cfg, d["slots"][0])
     n0, n1, n2 = names
@@ -319,18 +403,21 @@ def main():
         log(f"projection shader clock {ghz:.3f} GHz (median of {len(clocks)} launches' workgroup medians); "
             f"{rec['frac_at_clock']:.3f} of the MFMA peak at that clock")
 
-    # the dominant kernel (longest launch) carries the roofline object
-    dom = max(avg, key=avg.get)
+    # The dominant kernel carries the roofline object, at its average launch
+    # duration over the timed region.
     rd = kernels[dom]
     if rd["bound"] == "mfma":
-        roofline = {"bound": "mfma", "achieved": rd["achieved_TFLOPs"], "peak": BF16_MFMA_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": rd["frac"], "traffic": rd["traffic_bytes"], "kernel": dom}
+        achieved = rd["flops"] / (dom_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": rd["traffic_bytes"],
+                    "kernel": dom, "ms": dom_ms}
         if "clock_ghz" in rd:
             roofline["clock_ghz"] = rd["clock_ghz"]
-            roofline["frac_at_clock"] = rd["frac_at_clock"]
+            roofline["frac_at_clock"] = achieved / (BF16_MFMA_PEAK_TFLOPS * rd["clock_ghz"] / PEAK_CLOCK_GHZ)
     else:
-        roofline = {"bound": "hbm", "achieved": rd["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": rd["frac"], "traffic": rd["traffic_bytes"], "kernel": dom}
+        achieved = rd["bytes"] / (dom_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": rd["traffic_bytes"], "kernel": dom, "ms": dom_ms}
 
     rows_per_s = cfg.T * args.steps / wall
 
@@ -346,14 +433,14 @@ def main():
         for _ in range(warmup):
             run()
         total = 0.0
+        e0, e1 = timer.event(), timer.event()
         for _ in range(timed):
             torch.sum(flush_src, dim=0, out=flush_dst)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
+            timer.record(e0)
             run()
-            e1.record()
+            timer.record(e1)
             torch.cuda.synchronize()
-            total += e0.elapsed_time(e1)
+            total += timer.elapsed_ms(e0, e1)
         return total / timed
 
     # The ceiling of the norms' traffic: the norms kernel against its traffic
@@ -463,6 +550,7 @@ def main():
         "norms_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
+    timer.close()
     print(json.dumps(out), flush=True)
 
 

@@ -109,9 +109,12 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 // lane (global_load_lds_dwordx4, gfx950). Issued as inline assembly so the
 // kernel alone accounts for these writes with explicit vmcnt waits and
 // barriers (the pipeline below), instead of a conservative wait for every
-// outstanding load before each LDS read.
+// outstanding load before each LDS read. An LDS DMA that reads M0 right after
+// a scalar write of M0 needs one wait state in between (the compiler puts an
+// s_nop there for its own LDS DMA; nothing does inside an asm statement).
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+                 : "memory", "m0");
 }
 
 // A operand of the fused form: the layer-norm output built on the fly from
