@@ -149,7 +149,7 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
                                                               int64_t N, int32_t L, int32_t tiles_m, int32_t tiles_n,
                                                               int32_t total_tiles, FusedA fa, float* __restrict__ W,
                                                               int32_t k_split, uint64_t* __restrict__ stamps,
-                                                              int64_t stamps_len, bool layer_sync) {
+                                                              int64_t stamps_len, bool layer_sync, bool layer_inner) {
     using CF = Cfg<BM, BN, WM, WN>;
     // Clock stamps (diagnostic, stamps non-null): the shader clock counter
     // and the constant-rate counter when the workgroup starts; the wait keeps
@@ -188,11 +188,22 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
         const int t = (int)blockIdx.x + it * G;
         return t < total_tiles ? t : total_tiles;
     };
+    //
+    // layer_inner (fused form, unsplit, N <= 256): tile ids run over (M tile,
+    // layer, N tile) instead, so the layers of one h panel sit side by side
+    // under one L2 and the panel comes from memory once rather than once per
+    // layer (with N this narrow the layers' weights are small).
     int layer = 0, ks = 0;
     int64_t m0 = 0, n0 = 0;
     const int64_t k_len = SPLIT ? K / k_split : K;  // K walked per tile
     auto decode = [&](int tile) {
         const int tn = tile % tiles_n;
+        if (!SPLIT && layer_inner) {
+            layer = (tile / tiles_n) % L;
+            m0 = (int64_t)(tile / (tiles_n * L)) * BM;
+            n0 = (int64_t)tn * BN;
+            return;
+        }
         const int tm = (tile / tiles_n) % tiles_m;
         const int lt = tile / (tiles_n * tiles_m);
         layer = SPLIT ? lt % L : lt;
@@ -699,8 +710,12 @@ int launch_tiles(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
     // (edge workload, 268 MB: projection 6.22 -> 5.55 ms; the long
     // workload's 67 MB run 3.5% faster in the per-XCD layer order).
     const bool layer_sync = (int64_t)a.L * a.K * a.N * 2 > ((int64_t)128 << 20);
+    // H = 2 (N = 256): fused projection 0.301 -> 0.270 ms on the long
+    // workload's rows; neutral at N = 128.
+    const bool layer_inner = FUSED && !SPLIT && !layer_sync && a.N <= 256;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(CF::THREADS), lds_bytes, stream, a.A, a.B, a.C, a.M, a.K, a.N, a.L,
-                       tiles_m, tiles_n, total, fa, a.ws, SPLIT ? a.k_split : 1, a.stamps, a.stamps_len, layer_sync);
+                       tiles_m, tiles_n, total, fa, a.ws, SPLIT ? a.k_split : 1, a.stamps, a.stamps_len, layer_sync,
+                       layer_inner);
     if (a.workgroups) *a.workgroups = grid;
     return 0;
 }
@@ -750,11 +765,20 @@ int launch_reduce(const ProjectArgs& a, int cus, hipStream_t stream) {
 template <bool FUSED, bool PW, int CMODE, bool B_ND>
 int launch_shape(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
     // 256 x 256 tiles when they fill the chip, else 128 x 128, with K split
-    // when even those are too few (k_split > 1, unfused form only).
+    // when even those are too few (k_split > 1). The fused form takes
+    // 256 x 128 tiles (eight waves of 64 x 64) where those fill the chip and
+    // 256 x 256 ones do not (N = 128, a KV head per GPU: 0.234 -> 0.198 ms on
+    // the long workload's rows; the unfused form ran slower with them, 0.247
+    // against 0.210 ms).
     const int64_t big_tiles = (int64_t)a.L * ((a.M + 255) / 256) * (a.N / 256);
     const int cus = a.num_cus > 0 ? a.num_cus : 256;
     if (a.N % 256 == 0 && big_tiles >= cus)
         return launch_tiles<256, 256, 2, 4, FUSED, PW, CMODE, B_ND, false>(a, fa, stream);
+    if constexpr (FUSED) {
+        const int64_t wide_tiles = (int64_t)a.L * ((a.M + 255) / 256) * (a.N / 128);
+        if (a.k_split <= 1 && a.N % 128 == 0 && wide_tiles >= cus)
+            return launch_tiles<256, 128, 4, 2, FUSED, PW, CMODE, B_ND, false>(a, fa, stream);
+    }
     if (a.k_split > 1) {
         // 256 x 256 slices when the tile is not mostly empty rows (half
         // the operand traffic per flop of 128 x 128), else 128 x 128

@@ -1214,6 +1214,32 @@ def test_fused_project_parity_configs(nrc, oracle, name):
     assert ok, f"fused {name}: {msg}"
 
 
+@pytest.mark.parametrize("L,T,N", [(4, 16384, 128), (4, 16300, 128), (4, 16384, 256), (8, 8192, 128)])
+def test_fused_project_narrow_heads(nrc, oracle, L, T, N):
+    """A KV head or two per GPU at long-context sizes: the fused projection
+    on 256 x 128 tiles (N = 128; a ragged last row tile at T = 16300) and in
+    the layer-inner tile order (N <= 256) equals the norms followed by the
+    unfused projection bit for bit, and is within tolerance of the oracle on
+    sampled rows."""
+    from norm_rope_cache_amd import synth
+
+    lib = nrc._load()
+    assert lib.nrc_context_kv_project_workspace_bytes(L, T, 8192, N) == 0, "shape should not split"
+    x = synth.normal_bf16(7501 + T, (T, 8192))
+    hw = synth.normal_bf16(7502, (8192,), 1.0, 0.3)
+    pw = synth.normal_bf16(7503 + L, (L, 8192), 1.0, 0.3)
+    w = synth.normal_bf16(7504 + N, (L, 8192, N), std=0.02)
+    _say(f"fused narrow heads L={L} T={T} N={N}")
+    kv_u, kv_f = _fused_vs_unfused(nrc, x, hw, pw, w, L)
+    assert_bits_equal(kv_f, kv_u, f"fused vs unfused {L},{T},{N}")
+    del kv_u
+    rng = np.random.default_rng(T + N)
+    rows = np.unique(np.concatenate([[0, 255, 256, T - 1], rng.choice(T, 24, replace=False)]))
+    on = oracle.context_norms(np.ascontiguousarray(x[rows]), hw, pw, L)
+    ok, msg = projection_tolerance_ok(kv_f[:, rows], oracle.kv_project(on, w))
+    assert ok, f"fused narrow heads {L},{T},{N}: {msg}"
+
+
 @pytest.mark.parametrize("L,T,N", [(4, 512, 1024), (2, 16, 128), (2, 300, 384), (3, 700, 512), (4, 256, 1024)])
 def test_fused_split_matches_unfused_split(nrc, oracle, L, T, N):
     """The fused projection with its summation split (small T) equals the
