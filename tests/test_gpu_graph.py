@@ -1,0 +1,111 @@
+"""The chain's calls are asynchronous on the caller's stream and capturable
+into a graph, as the context page states for ContextNorms and
+ContextKvStore (a call is graph-capturable): the whole chain captured once
+into a HIP graph (torch.cuda.CUDAGraph) replays to the eager bits, replay
+after replay, with eager work and synchronisations between the replays."""
+
+import numpy as np
+import pytest
+
+from helpers import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def nrc():
+    import norm_rope_cache_amd as m
+
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    m._load()
+    return m
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+class _Chain:
+    """One buffer set of the chain on device: inputs, the stacked norms (or
+    the fused form's h and r), kv and the caches."""
+
+    def __init__(self, nrc, cfg, d, fused):
+        self.nrc, self.cfg, self.d, self.fused = nrc, cfg, d, fused
+        self.x = to_dev(d["x"])
+        self.hw = None if d["hidden_w"] is None else to_dev(d["hidden_w"])
+        self.pw = None if d["pre_w"] is None else to_dev(d["pre_w"])
+        self.w = to_dev(d["w_kv"])
+        self.pos = to_dev(d["positions"])
+        self.slots = to_dev(d["slots"][0])
+        self.cs = None if d["cos_sin"] is None else to_dev(d["cos_sin"])
+        self.caches0 = to_dev(d["caches"])
+        self.caches = self.caches0.clone()
+        self.kv = torch.empty((cfg.L, cfg.T, cfg.N), dtype=torch.bfloat16, device="cuda")
+        if fused:
+            self.h = torch.empty((cfg.T, 8192), dtype=torch.bfloat16, device="cuda")
+            self.r = torch.empty((cfg.T,), dtype=torch.float32, device="cuda")
+        else:
+            self.normed = torch.empty((cfg.L, cfg.T, 8192), dtype=torch.bfloat16, device="cuda")
+
+    def run(self):
+        nrc, cfg, d = self.nrc, self.cfg, self.d
+        if self.fused:
+            nrc.context_hidden_norm(self.x, self.hw, self.pw, cfg.L, d["hidden_eps"], d["pre_eps"], h=self.h, r=self.r)
+            nrc.context_kv_project_fused(self.h, self.r, self.pw, self.w, out=self.kv)
+        else:
+            nrc.context_norms(self.x, self.hw, self.pw, cfg.L, d["hidden_eps"], d["pre_eps"], out=self.normed)
+            nrc.context_kv_project(self.normed, self.w, out=self.kv)
+        nrc.context_kv_store(self.kv, self.pos, self.slots, self.cs, self.caches, cfg.H, d["k_eps"])
+
+    def reset(self):
+        self.caches.copy_(self.caches0)
+        self.kv.view(torch.int16).fill_(-1)
+
+
+@pytest.mark.parametrize("name,fused", [("tiny", False), ("prefill", False), ("prefill", True),
+                                        ("weightless", False)])
+def test_chain_replays_from_a_graph(nrc, name, fused):
+    """Eager chain -> reference kv and caches; the same calls captured into
+    a graph on a side stream; three replays, each from reset outputs, each
+    equal to the reference bit for bit, with an eager chain on a second
+    buffer set and a synchronisation between replays. Covers the split
+    projection (tiny, prefill: workspace from the graph's memory pool and a
+    second adding kernel), the one-pass projection (weightless) and the
+    fused form."""
+    from norm_rope_cache_amd import synth
+
+    cfg = synth.CONFIGS[name]
+    d = synth.make_inputs(cfg, with_cache=True)
+    _say(f"graph {name} fused={fused}: L={cfg.L} T={cfg.T} N={cfg.N}")
+    a, b = _Chain(nrc, cfg, d, fused), _Chain(nrc, cfg, d, fused)
+    a.reset()
+    a.run()
+    torch.cuda.synchronize()
+    ref_kv, ref_caches = to_host(a.kv), to_host(a.caches)
+    assert not np.array_equal(ref_caches, to_host(a.caches0)), "the chain wrote no cache cell"
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        a.reset()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            a.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        a.reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(a.kv), ref_kv), f"replay {rep}: kv differs from the eager chain"
+        assert np.array_equal(to_host(a.caches), ref_caches), f"replay {rep}: caches differ from the eager chain"
+        b.reset()
+        b.run()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(b.caches), ref_caches), f"eager chain after replay {rep} differs"
