@@ -2,7 +2,9 @@
 into a graph, as the context page states for ContextNorms and
 ContextKvStore (a call is graph-capturable): the whole chain captured once
 into a HIP graph (torch.cuda.CUDAGraph) replays to the eager bits, replay
-after replay, with eager work and synchronisations between the replays."""
+after replay, with eager work and synchronisations between the replays;
+and chains issued on two explicit streams at once each give the eager
+bits."""
 
 import numpy as np
 import pytest
@@ -109,3 +111,38 @@ def test_chain_replays_from_a_graph(nrc, name, fused):
         b.run()
         torch.cuda.synchronize()
         assert np.array_equal(to_host(b.caches), ref_caches), f"eager chain after replay {rep} differs"
+
+
+def test_chains_on_two_explicit_streams(nrc):
+    """Two buffer sets run the chain concurrently, each on its own stream
+    passed to every call (`stream=`), with the split projection's
+    workspace recorded on that stream; each equals the chain run on the
+    current stream, bit for bit."""
+    from norm_rope_cache_amd import synth
+
+    cfg = synth.CONFIGS["prefill"]
+    d = synth.make_inputs(cfg, with_cache=True)
+    ref = _Chain(nrc, cfg, d, False)
+    ref.reset()
+    ref.run()
+    torch.cuda.synchronize()
+    ref_kv, ref_caches = to_host(ref.kv), to_host(ref.caches)
+    del ref
+
+    sets = [_Chain(nrc, cfg, d, False) for _ in range(2)]
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    for c in sets:
+        c.reset()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for c, s in zip(sets, streams):
+            s.wait_stream(torch.cuda.current_stream())
+            nrc.context_norms(c.x, c.hw, c.pw, cfg.L, d["hidden_eps"], d["pre_eps"], out=c.normed, stream=s)
+            nrc.context_kv_project(c.normed, c.w, out=c.kv, stream=s)
+            nrc.context_kv_store(c.kv, c.pos, c.slots, c.cs, c.caches, cfg.H, d["k_eps"], stream=s)
+        torch.cuda.synchronize()
+        for i, c in enumerate(sets):
+            assert np.array_equal(to_host(c.kv), ref_kv), f"stream {i}, pass {rep}: kv differs"
+            assert np.array_equal(to_host(c.caches), ref_caches), f"stream {i}, pass {rep}: caches differ"
+            c.reset()
+        torch.cuda.synchronize()
