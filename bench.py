@@ -5,7 +5,10 @@ one stream, inputs and outputs resident in HBM. Default path: context_norms ->
 context_kv_project -> context_kv_store. --path fused times
 context_hidden_norm (hidden norm + per-row layer-norm scale) ->
 context_kv_project_fused (layer norms applied while staging the projection's
-A tiles) -> context_kv_store instead. The default workload is
+A tiles) -> context_kv_store instead; --path one-call times context_norms
+-> context_kv_project_store (the projection and the store in one call: for
+small T the store's kernel adds the split projection's partial sums). The
+default workload is
 the long-context configuration (L=4 draft layers, T=16384 rows, D=8192,
 H=8 KV heads, RoPE table [131072, 64], block size 16, 8192 blocks).
 
@@ -216,7 +219,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of the workload the CPU oracle is timed on (the whole chain on those rows); "
                          "default: every row, at most as many as hold the oracle's projection to 1.2 TFLOP")
-    ap.add_argument("--path", choices=("fused", "unfused"), default="unfused")
+    ap.add_argument("--path", choices=("fused", "unfused", "one-call"), default="unfused")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="KV heads to project and store (default: the workload's); e.g. 1 for the long workload's "
                          "per-GPU share under 8-way tensor parallelism, which splits the heads")
@@ -259,6 +262,7 @@ def main():
     positions = dv(d["positions"])
     slots = dv(d["slots"][0])  # the one slot mapping every layer shares
     fused = args.path == "fused"
+    one_call = args.path == "one-call"
     # Buffer sets the steps rotate over: a step whose touched bytes (rows in
     # and out, the projection weight, the written cache rows) fit twice in
     # the 256 MB infinity cache would otherwise find them there on the next
@@ -284,6 +288,7 @@ def main():
     torch.cuda.synchronize()
     log(f"{n_sets} buffer set(s), {touched / 1e6:.1f} MB touched per step")
     names = (["context_hidden_norm", "context_kv_project_fused", "context_kv_store"] if fused else
+             ["context_norms", "context_kv_project_store"] if one_call else
              ["context_norms", "context_kv_project", "context_kv_store"])
 
     step_no = [0]
@@ -311,6 +316,11 @@ def main():
         else:
             nrc.context_norms(b["x"], hw, pw, cfg.L, d["hidden_eps"], d["pre_eps"], out=b["normed"])
         mark(1)
+        if one_call:
+            nrc.context_kv_project_store(b["normed"], b["w"], positions, slots, cos_sin, b["caches"], d["k_eps"],
+                                         out=b["kv"])
+            mark(2)
+            return
         if fused:
             nrc.context_kv_project_fused(b["h"], b["r"], pw, b["w"], out=b["kv"])
         else:
@@ -364,15 +374,22 @@ def main():
         f"; timed region: wall/step {ms_step:.4f}, {dom} {dom_ms:.4f}")
 
     norms_b, store_b, flops = algorithmic_bytes(cfg, d["slots"][0])
-    n0, n1, n2 = names
+    n0, n1 = names[0], names[1]
     if fused:
         # pre-pass: read x, write h and r (plus the hidden weight once)
         norms_b = cfg.T * (2 * 8192 + 2 * 8192 + 4) + (2 * 8192 if cfg.hidden_weighted else 0)
     kernels = {
         n0: {"bound": "hbm", "ms": avg[n0], "bytes": norms_b, "achieved_GBs": norms_b / (avg[n0] * 1e-3) / 1e9},
         n1: {"bound": "mfma", "ms": avg[n1], "flops": flops, "achieved_TFLOPs": flops / (avg[n1] * 1e-3) / 1e12},
-        n2: {"bound": "hbm", "ms": avg[n2], "bytes": store_b, "achieved_GBs": store_b / (avg[n2] * 1e-3) / 1e9},
     }
+    if one_call:
+        # the call also does the store's work (its bytes below), rated here
+        # by the projection's flops alone
+        kernels[n1]["store_bytes"] = store_b
+    else:
+        n2 = names[2]
+        kernels[n2] = {"bound": "hbm", "ms": avg[n2], "bytes": store_b,
+                       "achieved_GBs": store_b / (avg[n2] * 1e-3) / 1e9}
     for k, rec in kernels.items():
         if rec["bound"] == "hbm":
             rec["frac"] = rec["achieved_GBs"] / HBM_PEAK_GBS
@@ -386,7 +403,7 @@ def main():
     # them). The MFMA peak is quoted at 2.4 GHz; under this load the chip
     # runs slower, and frac_at_clock rates the projection against the peak
     # scaled to the measured clock.
-    if not fused:
+    if not fused and not one_call:
         clocks = []
         for _ in range(10):
             b = sets[step_no[0] % n_sets]

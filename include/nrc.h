@@ -388,6 +388,38 @@ int32_t nrc_context_kv_store_ex(const uint16_t* k, const uint16_t* v, int64_t k_
                                 int64_t head_stride, int32_t H, int32_t L, float eps, void* stream);
 
 /*
+ * nrc_context_kv_project_store - the projection and the store of
+ * "...runtime.draft", ContextKV (_project, then store on the k/v views of the
+ * projection's own output) in one call, with the same results as
+ * nrc_context_kv_project_split followed by nrc_context_kv_store on
+ * k = kv, v = kv + H 64 (layer stride T N, row stride N), H = N / 128: kv
+ * and every cache cell bit for bit. Where the shape splits the summation,
+ * the slices are added by the store's kernel (slice order, one rounding to
+ * bf16, as nrc_context_kv_project_split adds them), which writes kv and
+ * inserts each row in the same pass; otherwise the one-pass projection runs,
+ * then the store.
+ *
+ *   normed, w, w_layout, kv, L, T, D, N, workspace, workspace_bytes
+ *              as nrc_context_kv_project_split (kv [L, T, N] is written,
+ *              every row).
+ *   positions, slots, rows, cos_sin, max_position, caches, num_blocks,
+ *   block_size, eps
+ *              as nrc_context_kv_store (slots and caches: host arrays of L
+ *              device pointers; rows <= T; caches contiguous
+ *              [num_blocks, H, block_size, 128]).
+ * Every operand is checked before anything is launched. Errors: those of
+ * both calls (N / 128 must be a power of two). rows == 0: the projection
+ * alone (slots, caches unused). T == 0: NRC_OK, nothing launched. Calls
+ * that share a workspace must not overlap.
+ */
+int32_t nrc_context_kv_project_store(const uint16_t* normed, const uint16_t* w, int32_t w_layout, uint16_t* kv,
+                                     int32_t L, int64_t T, int64_t D, int64_t N, void* workspace,
+                                     int64_t workspace_bytes, const int64_t* positions, const int64_t* const* slots,
+                                     int64_t rows, const uint16_t* cos_sin, int64_t max_position,
+                                     uint16_t* const* caches, int64_t num_blocks, int64_t block_size, float eps,
+                                     void* stream);
+
+/*
  * nrc_check_scalars - diagnostic: the device primitives every kernel uses,
  * applied elementwise to n FP32 values (device arrays), so that they can be
  * compared with a reference over all 2^32 inputs:

@@ -103,6 +103,10 @@ def _load():
     L.nrc_context_kv_store.argtypes = [
         _vp, _vp, _i64, _i64, _i64, _i64, _vp, ctypes.POINTER(_vp), _i64, _i64, _vp, _i64,
         ctypes.POINTER(_vp), _i64, _i64, _i32, _i32, _f32, _vp]
+    L.nrc_context_kv_project_store.restype = _i32
+    L.nrc_context_kv_project_store.argtypes = [
+        _vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, ctypes.POINTER(_vp), _i64, _vp, _i64,
+        ctypes.POINTER(_vp), _i64, _i64, _f32, _vp]
     L.nrc_context_hidden_norm.restype = _i32
     L.nrc_context_hidden_norm.argtypes = [_vp, _i64, _i64, _vp, _vp, _i32, _f32, _f32, _f32, _f32, _vp, _vp, _vp]
     L.nrc_context_kv_project_fused.restype = _i32
@@ -464,6 +468,84 @@ def kv_views(kv, H):
     return v5[:, :, 0], v5[:, :, 1]
 
 
+def _store_operands(kv_ref, L, T, H, positions, slots, cos_sin, caches, rows):
+    """Checks of the store's operands against the K/V source kv_ref ([L, T, ...]
+    on one device); returns the host pointer arrays and sizes the C ABI takes:
+    (slot_arr, cache_arr, n_rows, num_blocks, block_size, max_position)."""
+    import torch
+
+    # Per-layer pointers: a contiguous stacked tensor is addressed by its
+    # layer stride (no per-layer views); lists and other tensors layer by layer.
+    if isinstance(caches, torch.Tensor) and caches.dim() == 5 and caches.is_contiguous():
+        _bf16(caches, "cache")
+        _same_device(caches, kv_ref, "caches")
+        if caches.shape[0] != L:
+            raise ValueError("one cache and one slot mapping per layer")
+        if caches.shape[2] != H or caches.shape[4] != 2 * HEAD_DIM:
+            raise ValueError("caches must be [num_blocks, H, block_size, 128]")
+        nb, bs = caches.shape[1], caches.shape[3]
+        c_base, c_step = caches.data_ptr(), caches.stride(0) * 2
+        cache_ptrs = [c_base + i * c_step for i in range(L)]
+    else:
+        cache_list = list(caches) if not isinstance(caches, torch.Tensor) else [caches[i] for i in range(caches.shape[0])]
+        if len(cache_list) != L:
+            raise ValueError("one cache and one slot mapping per layer")
+        c0 = cache_list[0]
+        if c0.dim() != 4 or c0.shape[1] != H or c0.shape[3] != 2 * HEAD_DIM:
+            raise ValueError("caches must be [num_blocks, H, block_size, 128]")
+        nb, _, bs, _ = c0.shape
+        for c in cache_list:
+            _bf16(c, "cache")
+            _same_device(c, kv_ref, "caches")
+            if c.shape != c0.shape:
+                raise ValueError("all caches must have one shape")
+        cache_ptrs = [c.data_ptr() for c in cache_list]
+    if isinstance(slots, torch.Tensor) and slots.dim() == 1:
+        # one mapping shared by every layer: each layer's pointer is the same array
+        if slots.dtype != torch.int64 or not slots.is_contiguous():
+            raise ValueError("slots must be contiguous int64 [rows] tensors of one length")
+        _same_device(slots, kv_ref, "slots")
+        slot_len = slots.shape[0]
+        slot_ptrs = [slots.data_ptr()] * L
+    elif isinstance(slots, torch.Tensor) and slots.dim() == 2 and slots.is_contiguous():
+        if slots.dtype != torch.int64:
+            raise ValueError("slots must be contiguous int64 [rows] tensors of one length")
+        if slots.shape[0] != L:
+            raise ValueError("one cache and one slot mapping per layer")
+        _same_device(slots, kv_ref, "slots")
+        slot_len = slots.shape[1]
+        s_base, s_step = slots.data_ptr(), slots.stride(0) * 8
+        slot_ptrs = [s_base + i * s_step for i in range(L)]
+    else:
+        slot_list = list(slots) if not isinstance(slots, torch.Tensor) else [slots[i] for i in range(slots.shape[0])]
+        if len(slot_list) != L:
+            raise ValueError("one cache and one slot mapping per layer")
+        for s in slot_list:
+            if (not isinstance(s, torch.Tensor) or s.dtype != torch.int64 or s.dim() != 1 or not s.is_contiguous()
+                    or s.shape[0] != slot_list[0].shape[0]):
+                raise ValueError("slots must be contiguous int64 [rows] tensors of one length")
+            _same_device(s, kv_ref, "slots")
+        slot_len = slot_list[0].shape[0]
+        slot_ptrs = [s.data_ptr() for s in slot_list]
+    n_rows = slot_len if rows is None else int(rows)
+    if n_rows < 0 or n_rows > slot_len:
+        raise ValueError(f"rows = {n_rows} must lie in [0, {slot_len}] (the slot mapping's length)")
+    if cos_sin is not None:
+        _bf16(cos_sin, "cos_sin")
+        _same_device(cos_sin, kv_ref, "cos_sin")
+        if cos_sin.dim() != 2 or cos_sin.shape[1] != HEAD_DIM:
+            raise ValueError("cos_sin must be [max_position, 64]")
+        if positions is None or positions.dtype != torch.int64 or not positions.is_contiguous():
+            raise ValueError("positions must be a contiguous int64 tensor")
+        _same_device(positions, kv_ref, "positions")
+        if positions.shape[0] < n_rows:
+            raise ValueError("positions shorter than the inserted rows")
+    slot_arr = (_vp * L)(*slot_ptrs)
+    cache_arr = (_vp * L)(*cache_ptrs)
+    max_pos = 0 if cos_sin is None else cos_sin.shape[0]
+    return slot_arr, cache_arr, n_rows, nb, bs, max_pos
+
+
 def context_kv_store_ex(kv, positions, slots, cos_sin, caches, H, eps=1e-6, k=None, v=None, stream=None):
     """The store with per-layer slot lists and strided cache views, in place.
 
@@ -567,79 +649,42 @@ def context_kv_store(kv, positions, slots, cos_sin, caches, H, eps=1e-6, rows=No
         k_ptr, v_ptr = k.data_ptr(), v.data_ptr()
         k_ls, k_rs, v_ls, v_rs = k.stride(0), k.stride(1), v.stride(0), v.stride(1)
     kv_ref = kv if k is None else k
-    # Per-layer pointers: a contiguous stacked tensor is addressed by its
-    # layer stride (no per-layer views); lists and other tensors layer by layer.
-    if isinstance(caches, torch.Tensor) and caches.dim() == 5 and caches.is_contiguous():
-        _bf16(caches, "cache")
-        _same_device(caches, kv_ref, "caches")
-        if caches.shape[0] != L:
-            raise ValueError("one cache and one slot mapping per layer")
-        if caches.shape[2] != H or caches.shape[4] != 2 * HEAD_DIM:
-            raise ValueError("caches must be [num_blocks, H, block_size, 128]")
-        nb, bs = caches.shape[1], caches.shape[3]
-        c_base, c_step = caches.data_ptr(), caches.stride(0) * 2
-        cache_ptrs = [c_base + i * c_step for i in range(L)]
-    else:
-        cache_list = list(caches) if not isinstance(caches, torch.Tensor) else [caches[i] for i in range(caches.shape[0])]
-        if len(cache_list) != L:
-            raise ValueError("one cache and one slot mapping per layer")
-        c0 = cache_list[0]
-        if c0.dim() != 4 or c0.shape[1] != H or c0.shape[3] != 2 * HEAD_DIM:
-            raise ValueError("caches must be [num_blocks, H, block_size, 128]")
-        nb, _, bs, _ = c0.shape
-        for c in cache_list:
-            _bf16(c, "cache")
-            _same_device(c, kv_ref, "caches")
-            if c.shape != c0.shape:
-                raise ValueError("all caches must have one shape")
-        cache_ptrs = [c.data_ptr() for c in cache_list]
-    if isinstance(slots, torch.Tensor) and slots.dim() == 1:
-        # one mapping shared by every layer: each layer's pointer is the same array
-        if slots.dtype != torch.int64 or not slots.is_contiguous():
-            raise ValueError("slots must be contiguous int64 [rows] tensors of one length")
-        _same_device(slots, kv_ref, "slots")
-        slot_len = slots.shape[0]
-        slot_ptrs = [slots.data_ptr()] * L
-    elif isinstance(slots, torch.Tensor) and slots.dim() == 2 and slots.is_contiguous():
-        if slots.dtype != torch.int64:
-            raise ValueError("slots must be contiguous int64 [rows] tensors of one length")
-        if slots.shape[0] != L:
-            raise ValueError("one cache and one slot mapping per layer")
-        _same_device(slots, kv_ref, "slots")
-        slot_len = slots.shape[1]
-        s_base, s_step = slots.data_ptr(), slots.stride(0) * 8
-        slot_ptrs = [s_base + i * s_step for i in range(L)]
-    else:
-        slot_list = list(slots) if not isinstance(slots, torch.Tensor) else [slots[i] for i in range(slots.shape[0])]
-        if len(slot_list) != L:
-            raise ValueError("one cache and one slot mapping per layer")
-        for s in slot_list:
-            if (not isinstance(s, torch.Tensor) or s.dtype != torch.int64 or s.dim() != 1 or not s.is_contiguous()
-                    or s.shape[0] != slot_list[0].shape[0]):
-                raise ValueError("slots must be contiguous int64 [rows] tensors of one length")
-            _same_device(s, kv_ref, "slots")
-        slot_len = slot_list[0].shape[0]
-        slot_ptrs = [s.data_ptr() for s in slot_list]
-    n_rows = slot_len if rows is None else int(rows)
-    if n_rows < 0 or n_rows > slot_len:
-        raise ValueError(f"rows = {n_rows} must lie in [0, {slot_len}] (the slot mapping's length)")
-    if cos_sin is not None:
-        _bf16(cos_sin, "cos_sin")
-        _same_device(cos_sin, kv_ref, "cos_sin")
-        if cos_sin.dim() != 2 or cos_sin.shape[1] != HEAD_DIM:
-            raise ValueError("cos_sin must be [max_position, 64]")
-        if positions is None or positions.dtype != torch.int64 or not positions.is_contiguous():
-            raise ValueError("positions must be a contiguous int64 tensor")
-        _same_device(positions, kv_ref, "positions")
-        if positions.shape[0] < n_rows:
-            raise ValueError("positions shorter than the inserted rows")
-    slot_arr = (_vp * L)(*slot_ptrs)
-    cache_arr = (_vp * L)(*cache_ptrs)
-    max_pos = 0 if cos_sin is None else cos_sin.shape[0]
+    slot_arr, cache_arr, n_rows, nb, bs, max_pos = _store_operands(kv_ref, L, T, H, positions, slots, cos_sin,
+                                                                  caches, rows)
     _check(_load().nrc_context_kv_store(
         ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), k_ls, k_rs, v_ls, v_rs,
         _ptr(positions) if cos_sin is not None else None, slot_arr, n_rows, T, _ptr(cos_sin), max_pos, cache_arr,
         nb, bs, H, L, eps, _stream(stream)))
+
+
+def context_kv_project_store(normed, w_kv, positions, slots, cos_sin, caches, eps=1e-6, rows=None, out=None,
+                             stream=None, w_layout="dn"):
+    """context_kv_project (split=True) then context_kv_store on its output,
+    in one call: same kv and cache bits. Where the shape splits the
+    summation (small T), the store's kernel adds the slices itself, writing
+    kv and inserting each row in the same pass. H = N / 128. Returns kv."""
+    import torch
+
+    L, T, D, N, layout, out = _project_operands(normed, w_kv, out, w_layout)
+    if N % (2 * HEAD_DIM):
+        raise ValueError("N must be 2 H 64")
+    H = N // (2 * HEAD_DIM)
+    slot_arr, cache_arr, n_rows, nb, bs, max_pos = _store_operands(out, L, T, H, positions, slots, cos_sin, caches,
+                                                                  rows)
+    lib = _load()
+    need = lib.nrc_context_kv_project_workspace_bytes(L, T, D, N)
+    if need < 0:
+        _check(need)
+    ws = None
+    if need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=normed.device)
+        if stream is not None:
+            ws.record_stream(stream)
+    _check(lib.nrc_context_kv_project_store(
+        _ptr(normed), _ptr(w_kv), layout, _ptr(out), L, T, D, N, _ptr(ws), need,
+        _ptr(positions) if cos_sin is not None else None, slot_arr, n_rows, _ptr(cos_sin), max_pos, cache_arr, nb,
+        bs, eps, _stream(stream)))
+    return out
 
 
 def check_scalars(x, want_bf16=True, want_rsqrt=True, stream=None):

@@ -343,12 +343,24 @@ namespace {
 
 // The store behind both entry points: per-layer slot lists (NULL: the layer
 // stores nothing) of rows[l] entries, and a strided cache view.
+//
+// Sum mode (sum != NULL, the tail of nrc_context_kv_project_store): k and v
+// are the halves of the projection output kv [L, T, 2 H 64], which the
+// launches write, every row, from the split projection's partial sums
+// before inserting; launches happen even when no row is inserted.
+// check_only: validate the operands and launch nothing.
+struct SumSource {
+    const float* ws;  // [k_split, L, T, N] FP32 partial sums
+    int32_t k_split;
+    uint16_t* kv;     // [L, T, N]
+};
+
 int32_t store_impl(const char* what, const uint16_t* k, const uint16_t* v, int64_t k_layer_stride,
                    int64_t k_row_stride, int64_t v_layer_stride, int64_t v_row_stride, const int64_t* positions,
                    const int64_t* const* slots, const int64_t* rows, int64_t T, const uint16_t* cos_sin,
                    int64_t max_position, uint16_t* const* caches, int64_t num_blocks, int64_t block_size,
                    int64_t block_stride, int64_t page_stride, int64_t head_stride, int32_t H, int32_t L, float eps,
-                   void* stream) {
+                   void* stream, const SumSource* sum = nullptr, bool check_only = false) {
     if (L < 1) return fail(NRC_EINVAL, "%s: L = %d < 1", what, L);
     if (H < 1) return fail(NRC_EINVAL, "%s: H = %d < 1", what, H);
     if (H & (H - 1)) return fail(NRC_ENOTSUP, "%s: %d KV heads, not a power of two", what, H);
@@ -368,7 +380,11 @@ int32_t store_impl(const char* what, const uint16_t* k, const uint16_t* v, int64
     }
     if (max_rows * H > ((int64_t)1 << 25))
         return fail(NRC_ENOTSUP, "%s: rows x heads = %lld too large for one call", what, (long long)(max_rows * H));
-    if (max_rows == 0) return NRC_OK;
+    // sum mode: 8 lanes per (layer, row, 64 columns), up to 8 layers a launch,
+    // thread ids in 32 bits
+    if (sum && T * H > ((int64_t)1 << 24))
+        return fail(NRC_ENOTSUP, "%s: T x heads = %lld too large for one call", what, (long long)(T * H));
+    if (max_rows == 0 && (!sum || T == 0)) return NRC_OK;
     if (!k || !v) return fail(NRC_EINVAL, "%s: NULL k or v", what);
     if (!aligned(k, 16) || !aligned(v, 16)) return fail(NRC_EINVAL, "%s: k and v must be 16-byte aligned", what);
     if ((k_layer_stride | k_row_stride | v_layer_stride | v_row_stride) & 7)
@@ -391,6 +407,8 @@ int32_t store_impl(const char* what, const uint16_t* k, const uint16_t* v, int64
         if (!aligned(slots[l], 8) || !aligned(caches[l], 16))
             return fail(NRC_EINVAL, "%s: layer %d: slots must be 8-byte, cache 16-byte aligned", what, l);
     }
+
+    if (check_only) return NRC_OK;
 
     const uint32_t bs = (uint32_t)block_size;
     int32_t bs_shift = -1;
@@ -423,7 +441,15 @@ int32_t store_impl(const char* what, const uint16_t* k, const uint16_t* v, int64
             a.layers.rows[i] = live ? (uint32_t)rows[l] : 0u;
             if (a.layers.rows[i] > launch_rows) launch_rows = a.layers.rows[i];
         }
-        if (launch_rows == 0) continue;
+        if (launch_rows == 0 && !sum) continue;
+        if (sum) {
+            const int64_t layer_elems = T * 2 * H * NRC_HEAD_DIM;
+            a.ws = sum->ws + first * layer_elems;
+            a.ws_slice = (int64_t)L * layer_elems;
+            a.k_split = sum->k_split;
+            a.kv = sum->kv + first * layer_elems;
+            a.T = (uint32_t)T;
+        }
         a.layers_in_launch = (uint32_t)n;
         a.rows = launch_rows;
         a.H = (uint32_t)H;
@@ -466,6 +492,56 @@ int32_t nrc_context_kv_store(const uint16_t* k, const uint16_t* v, int64_t k_lay
     return store_impl("context_kv_store", k, v, k_layer_stride, k_row_stride, v_layer_stride, v_row_stride, positions,
                       rows > 0 ? slots : none, per_layer.data(), T, cos_sin, max_position, caches, num_blocks, block_size,
                       (int64_t)H * hs, 2 * NRC_HEAD_DIM, hs, H, rows > 0 ? L : 1, eps, stream);
+}
+
+int32_t nrc_context_kv_project_store(const uint16_t* normed, const uint16_t* w, int32_t w_layout, uint16_t* kv,
+                                     int32_t L, int64_t T, int64_t D, int64_t N, void* workspace,
+                                     int64_t workspace_bytes, const int64_t* positions, const int64_t* const* slots,
+                                     int64_t rows, const uint16_t* cos_sin, int64_t max_position,
+                                     uint16_t* const* caches, int64_t num_blocks, int64_t block_size, float eps,
+                                     void* stream) {
+    const char* what = "context_kv_project_store";
+    if (w_layout != NRC_KV_WEIGHT_DN && w_layout != NRC_KV_WEIGHT_ND)
+        return fail(NRC_EINVAL, "%s: weight layout %d (0 [L, D, N], 1 [L, N, D])", what, w_layout);
+    if (int32_t rc = project_shape_ok(L, T, D, N)) return rc;
+    if (T < 0 || rows < 0 || rows > T)
+        return fail(NRC_EINVAL, "%s: rows = %lld must lie in [0, T = %lld]", what, (long long)rows, (long long)T);
+    if (T == 0) return NRC_OK;
+    if (!normed || !w || !kv) return fail(NRC_EINVAL, "%s: NULL operand", what);
+    if (!aligned(normed, 16) || !aligned(w, 16) || !aligned(kv, 16))
+        return fail(NRC_EINVAL, "%s: operands must be 16-byte aligned", what);
+    const int64_t need = project_workspace_bytes(L, T, D, N);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+        return fail(NRC_EINVAL, "%s: needs a 16-byte aligned workspace of %lld bytes", what, (long long)need);
+    // no row inserted: the projection alone
+    if (rows == 0) return project_impl(normed, w, w_layout, kv, L, T, D, N, workspace, workspace_bytes, true, stream);
+
+    if (!slots || !caches) return fail(NRC_EINVAL, "%s: NULL slots or caches array", what);
+    for (int32_t l = 0; l < L; ++l)
+        if (!slots[l] || !caches[l]) return fail(NRC_EINVAL, "%s: NULL slots or cache of layer %d", what, l);
+    const int32_t H = (int32_t)(N / (2 * NRC_HEAD_DIM));
+    const int64_t hs = block_size * 2 * NRC_HEAD_DIM;
+    std::vector<int64_t> per_layer((size_t)L, rows);
+    nrc::ProjectArgs a{normed, w, kv, L, T, D, N, num_cus()};
+    a.b_nd = w_layout == NRC_KV_WEIGHT_ND;
+    SumSource sum{nullptr, 1, kv};
+    if (need > 0) {
+        a.ws = static_cast<float*>(workspace);
+        a.k_split = nrc::kv_project_k_split(L, T, D, N, a.num_cus);
+        a.leave_partials = true;
+        sum.ws = a.ws;
+        sum.k_split = a.k_split;
+    }
+    // every operand checked before anything is launched
+    auto store = [&](bool check_only) {
+        return store_impl(what, kv, kv + (int64_t)H * NRC_HEAD_DIM, T * N, N, T * N, N, positions, slots,
+                          per_layer.data(), T, cos_sin, max_position, caches, num_blocks, block_size,
+                          (int64_t)H * hs, 2 * NRC_HEAD_DIM, hs, H, L, eps, stream, need > 0 ? &sum : nullptr,
+                          check_only);
+    };
+    if (int32_t rc = store(true)) return rc;
+    if (int32_t rc = launch_status(nrc::launch_kv_project(a, (hipStream_t)stream), what)) return rc;
+    return store(false);
 }
 
 int32_t nrc_context_kv_store_ex(const uint16_t* k, const uint16_t* v, int64_t k_layer_stride, int64_t k_row_stride,

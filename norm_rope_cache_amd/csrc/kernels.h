@@ -48,6 +48,15 @@ struct KvStoreArgs {
     int64_t block_stride, page_stride, head_stride;  // cache view strides, elements
     uint32_t n_slots;
     float eps;
+    // Non-null: the launch also finishes a split projection - K and V come
+    // from the FP32 partial sums ws [k_split, L, T, N] (at this launch's first
+    // layer; ws_slice elements between slices), added in slice order and
+    // rounded into kv [L, T, N] (every row), instead of from k and v.
+    const float* ws = nullptr;
+    int64_t ws_slice = 0;
+    int32_t k_split = 0;
+    uint16_t* kv = nullptr;
+    uint32_t T = 0;
 };
 
 int launch_kv_store(const KvStoreArgs& a, hipStream_t stream);
@@ -115,6 +124,7 @@ struct ProjectArgs {
     bool b_nd = false;
     float* ws = nullptr;  // split K: FP32 partial sums [k_split, L, M, N]
     int32_t k_split = 1;
+    bool leave_partials = false;  // split K: stop after the sums (the store adds them)
     // Diagnostic clock stamps, 4 per workgroup (shader clock and constant-rate
     // clock at the start, then at the end), written when non-null; unfused,
     // unsplit form only. *workgroups receives the grid size when non-null.

@@ -786,7 +786,7 @@ int launch_shape(const ProjectArgs& a, const FusedA& fa, hipStream_t stream) {
                            ? launch_tiles<256, 256, 2, 4, FUSED, PW, CMODE, B_ND, true>(a, fa, stream)
                            : launch_tiles<128, 128, 2, 2, FUSED, PW, CMODE, B_ND, true>(a, fa, stream);
         if (rc) return rc;
-        return launch_reduce(a, cus, stream);
+        return a.leave_partials ? 0 : launch_reduce(a, cus, stream);
     }
     return launch_tiles<128, 128, 2, 2, FUSED, PW, CMODE, B_ND, false>(a, fa, stream);
 }

@@ -209,6 +209,111 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restric
     }
 }
 
+// The split projection's last step and the store in one pass: the FP32
+// partial sums of the S slices [S, L, T, N] (slice stride ws_slice
+// elements) are added in slice order and rounded to bf16 once - the same
+// operations and order as the projection's adding kernel, so kv gets the
+// same bits - and the result, written to kv [L, T, N], is at once the K or V
+// row part that the store inserts. One 8-lane group per (layer, row,
+// 64-wide column block c of the kv row): c < H is K head c, c >= H is V
+// head c - H, so the groups of a wave cover contiguous kv columns. Every row
+// of kv is written; rows at or past the layer's slot count, and rows whose
+// slot or position is out of range, insert nothing.
+template <int S, bool ROPE>
+__global__ __launch_bounds__(256) void kv_sum_store_kernel(
+    const float* __restrict__ ws, int64_t ws_slice, uint16_t* __restrict__ kv, uint32_t T, uint32_t H,
+    uint32_t log2_cols, uint32_t total_units, const int64_t* __restrict__ positions,
+    const uint16_t* __restrict__ cos_sin, int64_t max_position, StoreLayers layers, uint32_t block_size,
+    int32_t bs_shift, uint32_t n_slots, int64_t block_stride, int64_t page_stride, int64_t head_stride, float eps) {
+    const uint32_t unit = (blockIdx.x * blockDim.x + threadIdx.x) >> 3;
+    if (unit >= total_units) return;  // whole 8-lane groups leave together
+    const uint32_t g = threadIdx.x & 7u;
+    const uint32_t c = unit & ((1u << log2_cols) - 1u);
+    const uint32_t rt = unit >> log2_cols;  // l T + t
+    const uint32_t l = rt / T, t = rt - l * T;
+    uint32_t l_rows = 0;
+    uint64_t l_slots_a = 0, l_cache_a = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < (uint32_t)kMaxLayersPerLaunch; ++i) {
+        uint32_t ri = layers.rows[i];
+        uint64_t si = (uint64_t)(uintptr_t)layers.slots[i];
+        uint64_t ci = (uint64_t)(uintptr_t)layers.cache[i];
+        asm volatile("" : "+s"(ri), "+s"(si), "+s"(ci));
+        if (l == i) {
+            l_rows = ri;
+            l_slots_a = si;
+            l_cache_a = ci;
+        }
+    }
+    const bool insert = t < l_rows;
+    const bool is_k = c < H;
+    int64_t slot = -1, pos = 0;
+    if (insert) {
+        slot = ((const GlobalI64*)l_slots_a)[t];
+        if constexpr (ROPE) pos = positions[t];
+    }
+    const int64_t off = (int64_t)rt * ((int64_t)kHeadDim << log2_cols) + c * kHeadDim + 8 * g;
+    U32x4 lo[S], hi[S];
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+        lo[k] = load16(ws + (int64_t)k * ws_slice + off);
+        hi[k] = load16(ws + (int64_t)k * ws_slice + off + 4);
+    }
+    const bool slot_ok = (slot >= 0) & ((uint64_t)slot < (uint64_t)n_slots);
+    const bool pos_ok = !ROPE || ((pos >= 0) & (pos < max_position));
+    const bool store_row = insert & slot_ok & pos_ok;
+    // the cos/sin row of an inserted K head, fetched while the sums are in flight
+    uint2 cw = {0u, 0u}, sw = {0u, 0u};
+    if (ROPE && is_k && store_row) {
+        const uint16_t* cs = cos_sin + pos * kHeadDim;
+        cw = *reinterpret_cast<const uint2*>(cs + 4 * g);
+        sw = *reinterpret_cast<const uint2*>(cs + kHeadDim / 2 + 4 * g);
+    }
+    float acc[8] = {__uint_as_float(lo[0].x), __uint_as_float(lo[0].y), __uint_as_float(lo[0].z),
+                    __uint_as_float(lo[0].w), __uint_as_float(hi[0].x), __uint_as_float(hi[0].y),
+                    __uint_as_float(hi[0].z), __uint_as_float(hi[0].w)};
+#pragma unroll
+    for (int k = 1; k < S; ++k) {
+        const uint32_t p[8] = {lo[k].x, lo[k].y, lo[k].z, lo[k].w, hi[k].x, hi[k].y, hi[k].z, hi[k].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + __uint_as_float(p[e]);
+    }
+    const U32x4 w{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]), pack_bf16(acc[4], acc[5]),
+                  pack_bf16(acc[6], acc[7])};
+    store16(kv + off, w);
+
+    if (!store_row) return;
+    const uint32_t s32 = (uint32_t)slot;
+    uint32_t block, page;
+    if (bs_shift >= 0) {
+        block = s32 >> bs_shift;
+        page = s32 & (block_size - 1u);
+    } else {
+        block = s32 / block_size;
+        page = s32 - block * block_size;
+    }
+    const uint32_t h = is_k ? c : c - H;
+    GlobalU16* dst = (GlobalU16*)l_cache_a + (int64_t)block * block_stride + (int64_t)page * page_stride +
+                     (int64_t)h * head_stride + 8 * g;
+    if (is_k) {
+        store16_nt_global(dst, k_out<ROPE>(w, cw, sw, eps));
+    } else {
+        store16_nt_global(dst + kHeadDim, w);
+    }
+}
+
+template <int S>
+void launch_sum_store_s(const KvStoreArgs& a, hipStream_t stream) {
+    uint32_t log2_cols = 0;
+    while ((1u << log2_cols) != 2 * a.H) ++log2_cols;
+    const uint32_t total_units = a.layers_in_launch * a.T * 2 * a.H;
+    const dim3 grid((uint32_t)(((uint64_t)total_units * 8 + 255) / 256));
+    auto kernel = a.cos_sin ? kv_sum_store_kernel<S, true> : kv_sum_store_kernel<S, false>;
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a.ws, a.ws_slice, a.kv, a.T, a.H, log2_cols, total_units,
+                       a.positions, a.cos_sin, a.max_position, a.layers, a.block_size, a.bs_shift, a.n_slots,
+                       a.block_stride, a.page_stride, a.head_stride, a.eps);
+}
+
 template <bool ROPE>
 void launch_rope(const KvStoreArgs& a, uint32_t total_units, hipStream_t stream) {
     const uint32_t threads = 256;
@@ -230,6 +335,16 @@ void launch_rope(const KvStoreArgs& a, uint32_t total_units, hipStream_t stream)
 }
 
 int launch_kv_store(const KvStoreArgs& a, hipStream_t stream) {
+    if (a.ws) {
+        switch (a.k_split) {
+            case 2: launch_sum_store_s<2>(a, stream); break;
+            case 4: launch_sum_store_s<4>(a, stream); break;
+            case 8: launch_sum_store_s<8>(a, stream); break;
+            case 16: launch_sum_store_s<16>(a, stream); break;
+            default: return -1;
+        }
+        return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
     const uint32_t total_units = (uint32_t)a.layers_in_launch * a.rows * a.H;
     if (a.cos_sin)
         launch_rope<true>(a, total_units, stream);

@@ -245,6 +245,43 @@ def test_store_argument_checks(lib):
     assert _store(lib, rows=0, T=0) == 0
 
 
+def test_project_store_argument_checks(lib):
+    """The one-call projection + store checks the operands of both parts
+    before it launches anything (every call here fails, or does nothing, on
+    the host; the library assumes 256 CUs, so the 512-row shape splits)."""
+    f = lib.nrc_context_kv_project_store
+    need = 8 * 4 * 512 * 1024 * 4
+    arr = ctypes.c_void_p * 4
+    slots, caches = arr(*([0x20000] * 4)), arr(*([0x30000] * 4))
+
+    def call(**kw):
+        a = dict(normed=FAKE, w=FAKE, layout=0, kv=FAKE, L=4, T=512, D=8192, N=1024, ws=FAKE, wsb=need, pos=FAKE,
+                 slots=slots, rows=512, cs=FAKE, maxp=4096, caches=caches, nb=64, bs=16, eps=1e-6)
+        a.update(kw)
+        return f(a["normed"], a["w"], a["layout"], a["kv"], a["L"], a["T"], a["D"], a["N"], a["ws"], a["wsb"],
+                 a["pos"], a["slots"], a["rows"], a["cs"], a["maxp"], a["caches"], a["nb"], a["bs"], a["eps"], None)
+
+    assert call(layout=2) == EINVAL
+    assert call(N=1000) == ENOTSUP
+    assert call(rows=513) == EINVAL
+    assert call(rows=-1) == EINVAL
+    assert call(kv=MISALIGNED) == EINVAL
+    assert call(ws=None) == EINVAL
+    assert "workspace" in _err(lib)
+    assert call(wsb=need - 1) == EINVAL
+    assert call(slots=None) == EINVAL
+    assert call(slots=arr(0x20000, 0x20000, 0, 0x20000)) == EINVAL
+    assert "layer 2" in _err(lib)
+    assert call(caches=arr(0x30000, 0x30008, 0x30000, 0x30000)) == EINVAL  # misaligned cache of layer 1
+    assert call(pos=None) == EINVAL  # RoPE without positions
+    assert call(nb=0) == EINVAL
+    # N = 384: three KV heads, not a power of two (the projection alone would accept it)
+    need3 = lib.nrc_context_kv_project_workspace_bytes(4, 512, 8192, 384)
+    assert call(N=384, wsb=need3) == ENOTSUP
+    assert "power of two" in _err(lib)
+    assert call(normed=None, w=None, kv=None, T=0, rows=0, ws=None, wsb=0) == 0
+
+
 def test_fused_argument_checks(lib):
     f = lib.nrc_context_hidden_norm
     assert f(FAKE, 4, 4096, None, None, 1, 1e-6, 1e-6, 0.0, 0.0, FAKE, FAKE, None) == ENOTSUP

@@ -34,8 +34,8 @@ class _Chain:
     """One buffer set of the chain on device: inputs, the stacked norms (or
     the fused form's h and r), kv and the caches."""
 
-    def __init__(self, nrc, cfg, d, fused):
-        self.nrc, self.cfg, self.d, self.fused = nrc, cfg, d, fused
+    def __init__(self, nrc, cfg, d, fused, one_call=False):
+        self.nrc, self.cfg, self.d, self.fused, self.one_call = nrc, cfg, d, fused, one_call
         self.x = to_dev(d["x"])
         self.hw = None if d["hidden_w"] is None else to_dev(d["hidden_w"])
         self.pw = None if d["pre_w"] is None else to_dev(d["pre_w"])
@@ -54,6 +54,11 @@ class _Chain:
 
     def run(self):
         nrc, cfg, d = self.nrc, self.cfg, self.d
+        if self.one_call:
+            nrc.context_norms(self.x, self.hw, self.pw, cfg.L, d["hidden_eps"], d["pre_eps"], out=self.normed)
+            nrc.context_kv_project_store(self.normed, self.w, self.pos, self.slots, self.cs, self.caches,
+                                         d["k_eps"], out=self.kv)
+            return
         if self.fused:
             nrc.context_hidden_norm(self.x, self.hw, self.pw, cfg.L, d["hidden_eps"], d["pre_eps"], h=self.h, r=self.r)
             nrc.context_kv_project_fused(self.h, self.r, self.pw, self.w, out=self.kv)
@@ -67,26 +72,37 @@ class _Chain:
         self.kv.view(torch.int16).fill_(-1)
 
 
-@pytest.mark.parametrize("name,fused", [("tiny", False), ("prefill", False), ("prefill", True),
-                                        ("weightless", False)])
-def test_chain_replays_from_a_graph(nrc, name, fused):
+@pytest.mark.parametrize("name,fused,one_call", [("tiny", False, False), ("prefill", False, False),
+                                                 ("prefill", True, False), ("weightless", False, False),
+                                                 ("tiny", False, True), ("prefill", False, True)])
+def test_chain_replays_from_a_graph(nrc, name, fused, one_call):
     """Eager chain -> reference kv and caches; the same calls captured into
     a graph on a side stream; three replays, each from reset outputs, each
     equal to the reference bit for bit, with an eager chain on a second
     buffer set and a synchronisation between replays. Covers the split
     projection (tiny, prefill: workspace from the graph's memory pool and a
-    second adding kernel), the one-pass projection (weightless) and the
-    fused form."""
+    second adding kernel), the one-pass projection (weightless), the fused
+    form, and the projection + store in one call (its store kernel adding
+    the split's partial sums; its eager bits also equal to the three
+    calls')."""
     from norm_rope_cache_amd import synth
 
     cfg = synth.CONFIGS[name]
     d = synth.make_inputs(cfg, with_cache=True)
-    _say(f"graph {name} fused={fused}: L={cfg.L} T={cfg.T} N={cfg.N}")
-    a, b = _Chain(nrc, cfg, d, fused), _Chain(nrc, cfg, d, fused)
+    _say(f"graph {name} fused={fused} one_call={one_call}: L={cfg.L} T={cfg.T} N={cfg.N}")
+    a, b = _Chain(nrc, cfg, d, fused, one_call), _Chain(nrc, cfg, d, fused, one_call)
     a.reset()
     a.run()
     torch.cuda.synchronize()
     ref_kv, ref_caches = to_host(a.kv), to_host(a.caches)
+    if one_call:
+        three = _Chain(nrc, cfg, d, False)
+        three.reset()
+        three.run()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(three.kv), ref_kv), "one call: kv differs from the three calls"
+        assert np.array_equal(to_host(three.caches), ref_caches), "one call: caches differ from the three calls"
+        del three
     assert not np.array_equal(ref_caches, to_host(a.caches0)), "the chain wrote no cache cell"
 
     side = torch.cuda.Stream()
