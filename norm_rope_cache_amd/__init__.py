@@ -530,6 +530,8 @@ def _store_operands(kv_ref, L, T, H, positions, slots, cos_sin, caches, rows):
     n_rows = slot_len if rows is None else int(rows)
     if n_rows < 0 or n_rows > slot_len:
         raise ValueError(f"rows = {n_rows} must lie in [0, {slot_len}] (the slot mapping's length)")
+    if n_rows > T:
+        raise ValueError(f"rows = {n_rows} exceeds the {T} rows of kv")
     if cos_sin is not None:
         _bf16(cos_sin, "cos_sin")
         _same_device(cos_sin, kv_ref, "cos_sin")

@@ -209,7 +209,9 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const uint16_t* __restric
     }
 }
 
-// The split projection's last step and the store in one pass: the FP32
+// The split projection's last step and the store in one pass (page
+// "...runtime.draft", ContextKV: the store reads the k/v views of the
+// projection's own output, so it may take that output as it is formed): the FP32
 // partial sums of the S slices [S, L, T, N] (slice stride ws_slice
 // elements) are added in slice order and rounded to bf16 once - the same
 // operations and order as the projection's adding kernel, so kv gets the

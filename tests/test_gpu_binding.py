@@ -51,6 +51,33 @@ def test_store_refuses_host_slots_positions_and_long_rows(nrc):
     assert np.array_equal(to_host(caches), before), "a refused call wrote the cache"
 
 
+def test_project_store_refuses_host_operands_and_long_rows(nrc):
+    """The one-call projection + store checks the store's operands before
+    anything runs: nothing written to kv or the caches."""
+    from norm_rope_cache_amd import synth
+
+    kv, pos, slots, cs, caches, H = _store_operands()
+    L, T = kv.shape[0], kv.shape[1]
+    normed = to_dev(synth.normal_bf16(63, (L, T, 8192)))
+    w = to_dev(synth.normal_bf16(64, (L, 8192, 2 * H * 64), std=0.02))
+    out = torch.zeros_like(kv)
+    before = to_host(caches)
+    long_slots = torch.arange(T + 3, dtype=torch.int64)
+    cases = {
+        "host slots": dict(positions=pos.cuda(), slots=slots),
+        "host positions": dict(positions=pos, slots=slots.cuda()),
+        "rows beyond the mapping": dict(positions=pos.cuda(), slots=slots[:5].cuda(), rows=6),
+        "rows beyond T": dict(positions=long_slots.cuda(), slots=long_slots.cuda(), rows=T + 1),
+    }
+    for what, kw in cases.items():
+        with pytest.raises(ValueError):
+            nrc.context_kv_project_store(normed, w, kw["positions"], kw["slots"], cs, caches, rows=kw.get("rows"),
+                                         out=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(caches), before), "a refused call wrote the cache"
+    assert not bool(out.view(torch.int16).any()), "a refused call wrote kv"
+
+
 def test_store_ex_refuses_host_slots_and_positions(nrc):
     kv, pos, slots, cs, caches, H = _store_operands()
     before = to_host(caches)
