@@ -117,3 +117,41 @@ def test_project_store_no_rows_is_the_projection(nrc):
     torch.cuda.synchronize()
     assert_bits_equal(to_host(kv), to_host(nrc.context_kv_project(Ad, Bd)), "kv")
     assert_bits_equal(to_host(c), caches, "caches untouched")
+
+
+def test_project_store_special_values(nrc):
+    """Rows whose projection sums are NaN, +-Inf or overflow (normed rows with
+    Inf, NaN or values near the bf16 maximum) take the same path through the
+    store kernel that adds the slices as through the adding kernel and the
+    store: the same kv and cache bits (split shape, RoPE on and off)."""
+    from norm_rope_cache_amd import synth
+
+    L, T, H, bs, nb = 2, 300, 2, 16, 32
+    N = 2 * H * 64
+    A = synth.normal_bf16(7500, (L, T, 8192))
+    A[0, 3, 100] = 0x7F80          # +Inf
+    A[1, 7, 5] = 0xFF80            # -Inf
+    A[0, 11, 9] = 0x7FC1           # NaN
+    A[1, 13, :64] = 0x7F7F         # bf16 max: sums overflow
+    A[0, 17] = 0x8000              # an all -0.0 row
+    B = synth.normal_bf16(7501, (L, 8192, N), std=0.02)
+    rng = np.random.default_rng(7502)
+    slots = rng.permutation(nb * bs)[:T].astype(np.int64)
+    pos = rng.integers(0, 256, T).astype(np.int64)
+    caches = synth.random_bits_u16(7503, (L, nb, H, bs, 128))
+    Ad, Bd = to_dev(A), to_dev(B)
+    need = nrc._load().nrc_context_kv_project_workspace_bytes(L, T, 8192, N)
+    assert need > 0, "the shape must split"
+    for rope in (True, False):
+        _say(f"project+store special values rope={rope}")
+        tab = to_dev(synth.rope_table(256)) if rope else None
+        c_two, c_one = to_dev(caches), to_dev(caches)
+        kv_two = nrc.context_kv_project(Ad, Bd)
+        nrc.context_kv_store(kv_two, to_dev(pos), to_dev(slots), tab, c_two, H)
+        kv_one = nrc.context_kv_project_store(Ad, Bd, to_dev(pos), to_dev(slots), tab, c_one)
+        torch.cuda.synchronize()
+        kv_h = to_host(kv_one)
+        assert_bits_equal(kv_h, to_host(kv_two), f"kv rope={rope}")
+        assert_bits_equal(to_host(c_one), to_host(c_two), f"caches rope={rope}")
+        f = (kv_h.astype(np.uint32) << 16).view(np.float32)
+        assert np.isnan(f).any() and np.isinf(f).any(), "the inputs must reach NaN and Inf sums"
