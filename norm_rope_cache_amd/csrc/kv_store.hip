@@ -1,5 +1,7 @@
 // Weightless K-norm + GPT-J RoPE + paged-cache insert, all layers of a call
-// in one launch (up to 8 layers; the host splits more).
+// in one launch (up to 8 layers; the host splits more). A second kernel
+// (kv_sum_store_kernel, below) also finishes a split projection: it adds the
+// partial sums into kv and inserts the rows in the same pass.
 //
 // Follows the vLLM page "...cutedsl.draft.context": _ContextKvStoreKernel
 // (operands, rounding points, slot addressing), _sum_squares_64 (the 64-wide
