@@ -468,7 +468,7 @@ def main():
     if not args.no_ceiling:
         flush_src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
         twin_out = torch.empty((cfg.L, cfg.T, 8192), dtype=torch.bfloat16, device=dev)
-        staged = (1 if hw is not None else 0) + (cfg.L if pw is not None and cfg.L <= 8 else 0)
+        staged = (1 if hw is not None else 0) + (cfg.L if pw is not None and cfg.L <= 5 else 0)
         per_cu = 1 if staged * 16384 > 65536 else 2  # the norms' workgroups per CU
         nb = cfg.T * 2 * 8192
         runs = {

@@ -111,8 +111,8 @@ constexpr int kRowBytes = kHidden * 2;     // 16 KiB of bf16 weights per norm
 // workgroup in LDS as packed bf16 (hidden first, then each layer), so the
 // registers hold only the row in flight and its prefetched successor.
 //
-// WEIGHTS_IN_LDS: the layer weights fit in LDS (L <= 8); otherwise they are
-// read from memory per row (L2-resident).
+// WEIGHTS_IN_LDS: the layer weights are staged in LDS (up to 5 layers);
+// otherwise they are read from memory per row (L2-resident).
 // ADD_CENTER: gamma = w + center with an FP32 add per use; otherwise both
 // centers are +-0.0 and the add is folded into the staged weights (a -0.0
 // weight turns into +0.0 when its center is +0.0, the only case where
@@ -353,7 +353,12 @@ dim3 norms_grid(const NormsArgs& a, size_t lds) {
 }  // namespace
 
 int launch_context_norms(const NormsArgs& a, hipStream_t stream) {
-    const bool in_lds = a.L <= 8;
+    // Layer weights staged in LDS up to 5 layers; beyond, each row reads them
+    // from L2 and the workgroup stages only the hidden weight, so two
+    // workgroups share a CU instead of one (cold launches, same bits: edge
+    // workload, L = 8, 1016 -> 922 us; the long workload's rows at L = 6 and
+    // 8, 2% faster; at L = 5 1% slower, so 5 keeps LDS).
+    const bool in_lds = a.L <= 5;
     const size_t lds = (size_t)((a.hidden_w ? 1 : 0) + (a.pre_w && in_lds ? a.L : 0)) * kRowBytes;
     const dim3 grid = norms_grid(a, lds);
     // A center of exactly +0.0 or -0.0 folds into the bf16 weights.
