@@ -747,8 +747,8 @@ def context_kv_chain(x, hidden_w, pre_w, w_kv, positions, slots, cos_sin, caches
                      pre_eps=1e-6, k_eps=1e-6, fused=False, workspace=None, kv=None, stream=None, split=True):
     """The whole chain, in place on `caches`; returns kv [L, T, N].
 
-    fused=False (the faster form on MI355X): norms into `workspace`
-    ([L, T, 8192] bf16) -> projection -> store. fused=True: pre-pass (h, r)
+    fused=False (the faster form on MI355X at H = 8): norms into `workspace`
+    ([L, T, 8192] bf16) -> projection and store (one call with split=True). fused=True: pre-pass (h, r)
     -> fused projection -> store, without the [L, T, 8192] intermediate;
     `workspace` may be a tuple (h [T, 8192] bf16, r [T] float32). Both forms
     write the same bits for the same `split`; for small T split=True splits
@@ -761,6 +761,12 @@ def context_kv_chain(x, hidden_w, pre_w, w_kv, positions, slots, cos_sin, caches
         kv = context_kv_project_fused(h, r, pre_w, w_kv, out=kv, stream=stream, split=split)
     else:
         normed = context_norms(x, hidden_w, pre_w, L, hidden_eps, pre_eps, out=workspace, stream=stream)
+        if split:
+            # the projection and the store in one call (same bits as the two)
+            if w_kv.shape[2] != 2 * H * HEAD_DIM:
+                raise ValueError("w_kv must be [L, D, 2 H 64]")
+            return context_kv_project_store(normed, w_kv, positions, slots, cos_sin, caches, k_eps, out=kv,
+                                            stream=stream)
         kv = context_kv_project(normed, w_kv, out=kv, stream=stream, split=split)
     context_kv_store(kv, positions, slots, cos_sin, caches, H, k_eps, stream=stream)
     return kv
