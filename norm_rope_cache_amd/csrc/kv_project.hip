@@ -609,6 +609,13 @@ __global__ __launch_bounds__(64 * WM * WN) void kv_project_kernel(const uint16_t
             // previous stage's mid barrier, by which point their reads of
             // that buffer (stage st - 1, read during stage st - 2) were
             // consumed.
+            // A2, odd iteration: this iteration's DMA refills the pair buffer
+            // that holds stage st, whose fragments every wave read during the
+            // previous iteration; those reads complete before the barrier, so
+            // no DMA write can land on data a wave has yet to read (nothing
+            // else orders a wave's LDS reads against another wave's LDS DMA;
+            // measured cost within noise).
+            if constexpr (A2 && f == 1) wait_lgkmcnt0();
             if constexpr (!FUSED) barrier();
             if constexpr (FUSED) t_read(st + 1, b1);
 #pragma unroll
