@@ -142,7 +142,8 @@ def host_cpu():
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    # the machine's CPU share for one GPU is what OMP_NUM_THREADS says, if set
+    # a host shared between GPUs states each process's CPU share in
+    # OMP_NUM_THREADS; honour it when set
     omp = os.environ.get("OMP_NUM_THREADS", "")
     if omp.isdigit() and int(omp) > 0:
         n = min(n, int(omp))
