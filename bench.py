@@ -226,6 +226,9 @@ def main():
                          "per-GPU share under 8-way tensor parallelism, which splits the heads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device-to-device once, a known-size reference for HBM byte counters")
+    ap.add_argument("--hipblaslt", action="store_true",
+                    help="after the chain, time the projection against hipBLASLt (torch.mm per layer) on the same "
+                         "operands, the weight both as given ([L, D, N]) and K-contiguous ([L, N, D])")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -521,6 +524,29 @@ def main():
         del s_in, s_out, b_out, flush_src
         log("variants: " + ", ".join(f"{k}={v['ms']:.4f} ms" for k, v in variants.items()))
 
+    # The projection against hipBLASLt on the same rows (torch.mm per layer,
+    # plain 2-D products), each launch cold as in the chain; for the design
+    # notes' comparison, not part of the step.
+    blas = {}
+    if args.hipblaslt and not fused:
+        flush_src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
+        a_in = sets[0]["normed"]
+        nrc.context_norms(x, hw, pw, cfg.L, d["hidden_eps"], d["pre_eps"], out=a_in)
+        c_out = torch.empty((cfg.L, cfg.T, cfg.N), dtype=torch.bfloat16, device=dev)
+        w_nd = w_kv.transpose(1, 2).contiguous()  # [L, N, D]
+        runs = {
+            "context_kv_project [L, D, N]": lambda: nrc.context_kv_project(a_in, w_kv, out=c_out),
+            "context_kv_project [L, N, D]": lambda: nrc.context_kv_project(a_in, w_nd, out=c_out, w_layout="nd"),
+            "torch.mm [L, D, N]": lambda: [torch.mm(a_in[l], w_kv[l], out=c_out[l]) for l in range(cfg.L)],
+            "torch.mm [L, N, D]": lambda: [torch.mm(a_in[l], w_nd[l].t(), out=c_out[l]) for l in range(cfg.L)],
+        }
+        for name, run in runs.items():
+            ms = time_launches(run, flush_src)
+            blas[name] = {"ms": ms, "achieved_TFLOPs": flops / (ms * 1e-3) / 1e12,
+                          "frac": flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+        del flush_src, c_out, w_nd
+        log("projection vs hipBLASLt (cold): " + ", ".join(f"{k} {v['ms']:.4f} ms" for k, v in blas.items()))
+
     cpu = None
     if not args.no_cpu_baseline:
         per_row = 2 * cfg.L * 8192 * cfg.N  # projection flop per row, the oracle's dominant stage
@@ -568,6 +594,8 @@ def main():
         "norms_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
+    if blas:
+        out["hipblaslt"] = blas
     timer.close()
     print(json.dumps(out), flush=True)
 
