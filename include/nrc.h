@@ -16,7 +16,9 @@
  *     Host pointer arrays (slots, caches) are read during the call only.
  *   - `stream` is a hipStream_t (NULL: the null stream). Calls enqueue their
  *     kernels on it and return without synchronising; nothing is kept after
- *     the return.
+ *     the return. The current device (hipSetDevice) must be the GPU that
+ *     holds the operands and the stream: launch shapes follow its compute
+ *     unit count, and nrc_context_kv_project_noalloc uses its scratch.
  *   - Return value: NRC_OK (0) or a negative errno-style code. All argument
  *     checks finish before the first launch, so an error means nothing was
  *     enqueued. nrc_last_error() then describes it.

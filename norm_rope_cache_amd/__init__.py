@@ -138,12 +138,37 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _stream(stream, ref):
+    """The HIP stream for a call on ref's GPU: the given torch stream, which
+    must belong to that GPU, or that GPU's current stream."""
     import torch
 
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(ref.device)
+    elif stream.device != ref.device:
+        raise ValueError(f"stream is on {stream.device}, the operands on {ref.device}")
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _call(ref, fn, *args):
+    """One C-ABI call with ref's GPU as the current device (the library sizes
+    its launches and finds its scratch on the current device), raising
+    NrcError on a non-zero status."""
+    import torch
+
+    dev = ref.device.index
+    if dev is not None and dev != torch.cuda.current_device():
+        with torch.cuda.device(dev):
+            _check(fn(*args))
+    else:
+        _check(fn(*args))
+
+
+def _all_on(ref, **tensors):
+    """_same_device for every operand given (None: absent)."""
+    for name, t in tensors.items():
+        if t is not None:
+            _same_device(t, ref, name)
 
 
 def _bf16(t, name, contiguous=True):
@@ -193,8 +218,9 @@ def context_norms(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hidden_c
         _bf16(out, "out")
         if tuple(out.shape) != (L, T, D):
             raise ValueError("out must be [L, T, D]")
-    _check(_load().nrc_context_norms(_ptr(x), T, D, _ptr(hidden_w), _ptr(pre_w), L, hidden_eps, pre_eps,
-                                     hidden_center, pre_center, _ptr(out), _stream(stream)))
+    _all_on(x, hidden_w=hidden_w, pre_w=pre_w, out=out)
+    _call(x, _load().nrc_context_norms, _ptr(x), T, D, _ptr(hidden_w), _ptr(pre_w), L, hidden_eps, pre_eps,
+          hidden_center, pre_center, _ptr(out), _stream(stream, x))
     return out
 
 
@@ -236,9 +262,10 @@ def context_norms_ex(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hidde
         _bf16(out, "out")
         if tuple(out.shape) != (L, T, D):
             raise ValueError("out must be [L, T, D]")
+    _all_on(x, hidden_w=hidden_w, pre_w=pre_w, out=out)
     flags = (HIDDEN_INPUT_SCALE if hidden_input_scale else 0) | (PRE_INPUT_SCALE if pre_input_scale else 0)
-    _check(_load().nrc_context_norms_ex(_ptr(x), T, D, _ptr(hidden_w), hk, _ptr(pre_w), pk, L, hidden_eps, pre_eps,
-                                        hidden_center, pre_center, flags, _ptr(out), _stream(stream)))
+    _call(x, _load().nrc_context_norms_ex, _ptr(x), T, D, _ptr(hidden_w), hk, _ptr(pre_w), pk, L, hidden_eps, pre_eps,
+          hidden_center, pre_center, flags, _ptr(out), _stream(stream, x))
     return out
 
 
@@ -284,14 +311,22 @@ def draft_boundary(branch, stream_in, alpha, beta, post_w=None, pre_w=None, post
     qk = _boundary_kind(pre_w, "pre_w")
     if out is None:
         out = torch.empty((m, D), dtype=torch.bfloat16, device=branch.device)
-    if store_stream and stream_out is None:
-        stream_out = torch.empty((m, D), dtype=torch.float32, device=branch.device)
+    else:
+        _bf16(out, "out")
+        if tuple(out.shape) != (m, D):
+            raise ValueError("out must be [m, 8192] like the branch")
     if not store_stream:
         stream_out = None
+    elif stream_out is None:
+        stream_out = torch.empty((m, D), dtype=torch.float32, device=branch.device)
+    elif stream_out.dtype != torch.float32 or tuple(stream_out.shape) != (m, D) or not stream_out.is_contiguous():
+        raise ValueError("stream_out must be a contiguous float32 [m, 8192] tensor")
+    _all_on(branch, stream_in=stream_in, alpha=alpha, beta=beta, post_w=post_w, pre_w=pre_w, out=out,
+            stream_out=stream_out)
     flags = (1 if post_input_scale else 0) | (2 if pre_input_scale else 0)
-    _check(_load().nrc_draft_boundary(_ptr(branch), m, D, _ptr(stream_in), sk, _ptr(alpha), _ptr(beta),
-                                      _ptr(post_w), pk, _ptr(pre_w), qk, post_eps, pre_eps, post_center, pre_center,
-                                      flags, _ptr(stream_out), _ptr(out), _stream(stream)))
+    _call(branch, _load().nrc_draft_boundary, _ptr(branch), m, D, _ptr(stream_in), sk, _ptr(alpha), _ptr(beta),
+          _ptr(post_w), pk, _ptr(pre_w), qk, post_eps, pre_eps, post_center, pre_center, flags, _ptr(stream_out),
+          _ptr(out), _stream(stream, branch))
     return stream_out, out
 
 
@@ -301,13 +336,18 @@ def context_hidden_norm(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hi
     import torch
 
     _bf16(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [T, 8192]")
     T, D = x.shape
     if hidden_w is not None:
         _bf16(hidden_w, "hidden_w")
+        if tuple(hidden_w.shape) != (D,):
+            raise ValueError("hidden_w must be [D]")
     if pre_w is not None:
         _bf16(pre_w, "pre_w")
         if tuple(pre_w.shape) != (L, D):
             raise ValueError("pre_w must be [L, D]")
+    _all_on(x, hidden_w=hidden_w, pre_w=pre_w)
     if h is None:
         h = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
     if r is None:
@@ -317,8 +357,8 @@ def context_hidden_norm(x, hidden_w, pre_w, L, hidden_eps=1e-6, pre_eps=1e-6, hi
         raise ValueError("h must be [T, D] bf16 and r [T] float32")
     _same_device(h, x, "h")
     _same_device(r, x, "r")
-    _check(_load().nrc_context_hidden_norm(_ptr(x), T, D, _ptr(hidden_w), _ptr(pre_w), L, hidden_eps, pre_eps,
-                                           hidden_center, pre_center, _ptr(h), _ptr(r), _stream(stream)))
+    _call(x, _load().nrc_context_hidden_norm, _ptr(x), T, D, _ptr(hidden_w), _ptr(pre_w), L, hidden_eps, pre_eps,
+          hidden_center, pre_center, _ptr(h), _ptr(r), _stream(stream, x))
     return h, r
 
 
@@ -331,6 +371,8 @@ def context_kv_project_fused(h, r, pre_w, w_kv, pre_center=0.0, out=None, stream
 
     _bf16(h, "h")
     _bf16(w_kv, "w_kv")
+    if h.dim() != 2 or w_kv.dim() != 3:
+        raise ValueError("h must be [T, D] and w_kv [L, D, N]")
     T, D = h.shape
     L, Dw, N = w_kv.shape
     if Dw != D:
@@ -360,11 +402,11 @@ def context_kv_project_fused(h, r, pre_w, w_kv, pre_center=0.0, out=None, stream
         ws = torch.empty(need, dtype=torch.uint8, device=h.device)
         if stream is not None:
             ws.record_stream(stream)  # the allocator may reuse it only after this stream's work
-        _check(lib.nrc_context_kv_project_fused_split(_ptr(h), _ptr(r), _ptr(pre_w), pre_center, _ptr(w_kv), _ptr(out),
-                                                      L, T, D, N, _ptr(ws), need, _stream(stream)))
+        _call(h, lib.nrc_context_kv_project_fused_split, _ptr(h), _ptr(r), _ptr(pre_w), pre_center, _ptr(w_kv),
+              _ptr(out), L, T, D, N, _ptr(ws), need, _stream(stream, h))
     else:
-        _check(lib.nrc_context_kv_project_fused(_ptr(h), _ptr(r), _ptr(pre_w), pre_center, _ptr(w_kv), _ptr(out), L,
-                                                    T, D, N, _stream(stream)))
+        _call(h, lib.nrc_context_kv_project_fused, _ptr(h), _ptr(r), _ptr(pre_w), pre_center, _ptr(w_kv), _ptr(out), L,
+              T, D, N, _stream(stream, h))
     return out
 
 
@@ -375,6 +417,8 @@ def _project_operands(normed, w_kv, out, w_layout):
     _bf16(normed, "normed")
     _bf16(w_kv, "w_kv")
     _same_device(w_kv, normed, "w_kv")
+    if normed.dim() != 3:
+        raise ValueError("normed must be [L, T, D]")
     L, T, D = normed.shape
     if w_layout == "dn":
         if w_kv.dim() != 3 or w_kv.shape[0] != L or w_kv.shape[1] != D:
@@ -413,12 +457,14 @@ def context_kv_project(normed, w_kv, out=None, stream=None, w_layout="dn", split
         ws = torch.empty(need, dtype=torch.uint8, device=normed.device)
         if stream is not None:
             ws.record_stream(stream)  # the allocator may reuse it only after this stream's work
-        _check(lib.nrc_context_kv_project_split(_ptr(normed), _ptr(w_kv), layout, _ptr(out), L, T, D, N, _ptr(ws),
-                                                need, _stream(stream)))
+        _call(normed, lib.nrc_context_kv_project_split, _ptr(normed), _ptr(w_kv), layout, _ptr(out), L, T, D, N,
+              _ptr(ws), need, _stream(stream, normed))
     elif w_layout == "dn":
-        _check(lib.nrc_context_kv_project(_ptr(normed), _ptr(w_kv), _ptr(out), L, T, D, N, _stream(stream)))
+        _call(normed, lib.nrc_context_kv_project, _ptr(normed), _ptr(w_kv), _ptr(out), L, T, D, N,
+              _stream(stream, normed))
     else:
-        _check(lib.nrc_context_kv_project_ex(_ptr(normed), _ptr(w_kv), 1, _ptr(out), L, T, D, N, _stream(stream)))
+        _call(normed, lib.nrc_context_kv_project_ex, _ptr(normed), _ptr(w_kv), 1, _ptr(out), L, T, D, N,
+              _stream(stream, normed))
     return out
 
 
@@ -431,8 +477,8 @@ def context_kv_project_noalloc(normed, w_kv, out, stream=None, w_layout="dn"):
     if out is None:
         raise ValueError("context_kv_project_noalloc writes into a caller-owned out")
     L, T, D, N, layout, out = _project_operands(normed, w_kv, out, w_layout)
-    _check(_load().nrc_context_kv_project_noalloc(_ptr(normed), _ptr(w_kv), layout, _ptr(out), L, T, D, N,
-                                                  _stream(stream)))
+    _call(normed, _load().nrc_context_kv_project_noalloc, _ptr(normed), _ptr(w_kv), layout, _ptr(out), L, T, D, N,
+          _stream(stream, normed))
     return out
 
 
@@ -451,8 +497,8 @@ def context_kv_project_timed(normed, w_kv, out=None, stream=None, w_layout="dn")
     n = 8 * torch.cuda.get_device_properties(normed.device).multi_processor_count
     stamps = torch.zeros(n, dtype=torch.int64, device=normed.device)
     wg, khz = ctypes.c_int32(0), ctypes.c_int32(0)
-    _check(lib.nrc_context_kv_project_timed(_ptr(normed), _ptr(w_kv), layout, _ptr(out), L, T, D, N, _ptr(stamps),
-                                            n, ctypes.byref(wg), ctypes.byref(khz), _stream(stream)))
+    _call(normed, lib.nrc_context_kv_project_timed, _ptr(normed), _ptr(w_kv), layout, _ptr(out), L, T, D, N,
+          _ptr(stamps), n, ctypes.byref(wg), ctypes.byref(khz), _stream(stream, normed))
     torch.cuda.synchronize(normed.device)
     st = stamps[: 4 * wg.value].view(-1, 4).cpu()
     ds = (st[:, 2] - st[:, 0]).double()
@@ -608,10 +654,9 @@ def context_kv_store_ex(kv, positions, slots, cos_sin, caches, H, eps=1e-6, k=No
                             for s, c in zip(slot_list, cache_list)])
     row_arr = (ctypes.c_int64 * L)(*rows)
     max_pos = 0 if cos_sin is None else cos_sin.shape[0]
-    _check(_load().nrc_context_kv_store_ex(
-        _ptr(k), _ptr(v), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
-        _ptr(positions) if cos_sin is not None else None, slot_arr, row_arr, T, _ptr(cos_sin), max_pos, cache_arr,
-        nb, bs, c0.stride(0), c0.stride(2), c0.stride(1), H, L, eps, _stream(stream)))
+    _call(k, _load().nrc_context_kv_store_ex, _ptr(k), _ptr(v), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
+          _ptr(positions) if cos_sin is not None else None, slot_arr, row_arr, T, _ptr(cos_sin), max_pos, cache_arr, nb,
+          bs, c0.stride(0), c0.stride(2), c0.stride(1), H, L, eps, _stream(stream, k))
 
 
 def context_kv_store(kv, positions, slots, cos_sin, caches, H, eps=1e-6, rows=None, k=None, v=None,
@@ -653,10 +698,9 @@ def context_kv_store(kv, positions, slots, cos_sin, caches, H, eps=1e-6, rows=No
     kv_ref = kv if k is None else k
     slot_arr, cache_arr, n_rows, nb, bs, max_pos = _store_operands(kv_ref, L, T, H, positions, slots, cos_sin,
                                                                   caches, rows)
-    _check(_load().nrc_context_kv_store(
-        ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), k_ls, k_rs, v_ls, v_rs,
-        _ptr(positions) if cos_sin is not None else None, slot_arr, n_rows, T, _ptr(cos_sin), max_pos, cache_arr,
-        nb, bs, H, L, eps, _stream(stream)))
+    _call(kv_ref, _load().nrc_context_kv_store, ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), k_ls, k_rs, v_ls, v_rs,
+          _ptr(positions) if cos_sin is not None else None, slot_arr, n_rows, T, _ptr(cos_sin), max_pos, cache_arr, nb,
+          bs, H, L, eps, _stream(stream, kv_ref))
 
 
 def context_kv_project_store(normed, w_kv, positions, slots, cos_sin, caches, eps=1e-6, rows=None, out=None,
@@ -682,10 +726,9 @@ def context_kv_project_store(normed, w_kv, positions, slots, cos_sin, caches, ep
         ws = torch.empty(need, dtype=torch.uint8, device=normed.device)
         if stream is not None:
             ws.record_stream(stream)
-    _check(lib.nrc_context_kv_project_store(
-        _ptr(normed), _ptr(w_kv), layout, _ptr(out), L, T, D, N, _ptr(ws), need,
-        _ptr(positions) if cos_sin is not None else None, slot_arr, n_rows, _ptr(cos_sin), max_pos, cache_arr, nb,
-        bs, eps, _stream(stream)))
+    _call(normed, lib.nrc_context_kv_project_store, _ptr(normed), _ptr(w_kv), layout, _ptr(out), L, T, D, N, _ptr(ws),
+          need, _ptr(positions) if cos_sin is not None else None, slot_arr, n_rows, _ptr(cos_sin), max_pos, cache_arr,
+          nb, bs, eps, _stream(stream, normed))
     return out
 
 
@@ -698,7 +741,7 @@ def check_scalars(x, want_bf16=True, want_rsqrt=True, stream=None):
         raise TypeError("x must be a contiguous float32 GPU tensor")
     bf = torch.empty(x.shape, dtype=torch.int16, device=x.device) if want_bf16 else None
     rs = torch.empty_like(x) if want_rsqrt else None
-    _check(_load().nrc_check_scalars(_ptr(x), _ptr(bf), _ptr(rs), x.numel(), _stream(stream)))
+    _call(x, _load().nrc_check_scalars, _ptr(x), _ptr(bf), _ptr(rs), x.numel(), _stream(stream, x))
     return bf, rs
 
 
@@ -710,7 +753,7 @@ def check_bf16_pair(x, stream=None):
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
         raise TypeError("x must be a contiguous float32 GPU tensor")
     out = torch.empty(x.shape, dtype=torch.int16, device=x.device)
-    _check(_load().nrc_check_bf16_pair(_ptr(x), _ptr(out), x.numel(), _stream(stream)))
+    _call(x, _load().nrc_check_bf16_pair, _ptr(x), _ptr(out), x.numel(), _stream(stream, x))
     return out
 
 
@@ -738,8 +781,8 @@ def traffic_twin(x, L, mode, out=None, per_cu=1, stream=None):
     if mode == TWIN_READS_ONLY:
         n = per_cu * torch.cuda.get_device_properties(x.device).multi_processor_count * 1024
         sink = torch.empty(n, dtype=torch.int32, device=x.device)
-    _check(_load().nrc_traffic_twin(_ptr(x), T, L, mode, per_cu, _ptr(out), _ptr(sink),
-                                    0 if sink is None else sink.numel(), _stream(stream)))
+    _call(x, _load().nrc_traffic_twin, _ptr(x), T, L, mode, per_cu, _ptr(out), _ptr(sink),
+          0 if sink is None else sink.numel(), _stream(stream, x))
     return out
 
 

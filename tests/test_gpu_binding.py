@@ -121,3 +121,51 @@ def test_shared_slot_mapping_equals_stacked_copies(nrc):
     torch.cuda.synchronize()
     assert np.array_equal(to_host(a), to_host(b))
     assert not np.array_equal(to_host(a), to_host(caches))
+
+
+def test_norm_bindings_refuse_misshaped_and_host_operands(nrc):
+    """Every operand the norm kernels read or write is checked for shape and
+    device before a launch: a short weight or output would otherwise be read
+    or written past its end."""
+    from norm_rope_cache_amd import synth
+
+    T, L = 3, 2
+    x = to_dev(synth.normal_bf16(71, (T, 8192)))
+    hw = to_dev(synth.normal_bf16(72, (8192,), mean=1.0, std=0.1))
+    pw = to_dev(synth.normal_bf16(73, (L, 8192), mean=1.0, std=0.1))
+    h = torch.zeros((T, 8192), dtype=torch.bfloat16, device="cuda")
+    r = torch.zeros((T,), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        nrc.context_hidden_norm(x, hw[:4096], pw, L, h=h, r=r)
+    with pytest.raises((TypeError, ValueError)):
+        nrc.context_hidden_norm(x, hw.cpu(), pw, L, h=h, r=r)
+    with pytest.raises(ValueError):
+        nrc.context_hidden_norm(x[0], hw, pw, L, h=h, r=r)
+    out = torch.zeros((L, T, 8192), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises((TypeError, ValueError)):
+        nrc.context_norms(x, hw, pw, L, out=out.cpu())
+    with pytest.raises((TypeError, ValueError)):
+        nrc.context_norms_ex(x, hw.float().cpu(), pw, L, out=out)
+
+    branch = to_dev(synth.normal_bf16(74, (T, 8192)))
+    s_in = torch.zeros((T, 8192), dtype=torch.float32, device="cuda")
+    alpha = torch.ones(8192, dtype=torch.float32, device="cuda")
+    beta = torch.ones(8192, dtype=torch.float32, device="cuda")
+    b_out = torch.zeros((T, 8192), dtype=torch.bfloat16, device="cuda")
+    s_out = torch.zeros((T, 8192), dtype=torch.float32, device="cuda")
+    cases = {
+        "short out": dict(out=b_out[:1]),
+        "float32 out": dict(out=s_out),
+        "short stream_out": dict(out=b_out, stream_out=s_out[:1]),
+        "bf16 stream_out": dict(out=b_out, stream_out=b_out),
+        "host stream_out": dict(out=b_out, stream_out=s_out.cpu()),
+        "host alpha": dict(out=b_out, alpha=alpha.cpu()),
+    }
+    for what, kw in cases.items():
+        a = kw.pop("alpha", alpha)
+        with pytest.raises((TypeError, ValueError)):
+            nrc.draft_boundary(branch, s_in, a, beta, hw, hw, **kw)
+    torch.cuda.synchronize()
+    for t in (h, r, out, b_out, s_out):
+        assert not bool(t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).any()), \
+            "a refused call wrote an output"
